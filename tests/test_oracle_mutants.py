@@ -1,0 +1,107 @@
+"""The oracle's pins must catch plausible mistakes in the oracle.
+
+Each case copies oracle.cpp, plants one mistake (a dropped term, a wrong
+sign, a wrong index, a transposed operand, a wrong rounding), builds the
+copy with the same flags, and runs the fast pins against it: at least one
+must fail. The planted mistakes live only in the temporary copies.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as oracle_pkg
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "drop_last_token_in_pv": ("for (int t = 0; t < L; ++t) acc +=", "for (int t = 0; t < L - 1; ++t) acc +="),
+    "exp_sign_flipped": ("std::exp(s[(size_t)t] - m)", "std::exp(m - s[(size_t)t])"),
+    "no_max_shift": ("std::exp(s[(size_t)t] - m)", "std::exp(s[(size_t)t])"),
+    "min_instead_of_max": ("if (s[(size_t)t] > m) m", "if (s[(size_t)t] < m) m"),
+    "scale_dropped": ("s[(size_t)t] = scale * dot;", "s[(size_t)t] = dot;"),
+    "no_normalisation": ("o[d] = acc / l;", "o[d] = acc;"),
+    "denominator_not_summed": ("l += p[(size_t)t];", "l = p[(size_t)t];"),
+    "group_mapping_modulo": ("h = (int)(item % Hq), g = h / nrep;", "h = (int)(item % Hq), g = h % Hkv;"),
+    "table_index_modulo": ("return k_pool[k_index(table[t / bs]", "return k_pool[k_index(table[t % bs]"),
+    "k_slot_channel_swapped": ("(size_t)t * 8 +\n           (size_t)(d % 8);", "(size_t)(d % 8) * 8 +\n           (size_t)t;"),
+    "v_layout_transposed": (
+        "((size_t)(blk * Hkv + g) * (size_t)D + (size_t)d) * (size_t)bs + (size_t)t;",
+        "((size_t)(blk * Hkv + g) * (size_t)bs + (size_t)t) * (size_t)D + (size_t)d;",
+    ),
+    "query_row_from_kv_head": ("q + ((size_t)b * Hq + h) * D, seq_lens[b]", "q + ((size_t)b * Hq + g) * D, seq_lens[b]"),
+    "append_slot_off_by_one": ("const int slot = pos % bs;", "const int slot = (pos + 1) % bs;"),
+    "append_position_is_length": ("const int pos = L - 1;", "const int pos = L - 2 + (L == 1);"),
+    "subnormal_scale": ("5.9604644775390625e-08f", "1.1920928955078125e-07f"),
+    "exponent_bias": ("((expo - 15 + 127) << 23)", "((expo - 14 + 127) << 23)"),
+    "round_half_up": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;", "if (rem >= 0x1000u) h += 1;"),
+}
+
+FAST_PINS = [
+    (pins.test_half_to_float_all_patterns, {}),
+    (pins.test_float_to_half_rne, {}),
+    (pins.test_paged_matches_float64_dense, {"name": "tiny"}),
+    (pins.test_paged_matches_float64_dense, {"name": "mixed_small"}),
+    (pins.test_paged_matches_float64_dense, {"name": "bs16_small"}),
+    (pins.test_single_token_returns_v0, {}),
+    (pins.test_two_tokens_logistic, {}),
+    (pins.test_dominant_key_without_overflow, {}),
+    (pins.test_all_scores_very_negative, {}),
+    (pins.test_query_head_to_kv_head_mapping, {}),
+    (pins.test_block_relabelling_invariance, {}),
+    (pins.test_kv_append_matches_numpy_scatter, {"cfg": "tiny"}),
+    (pins.test_kv_append_then_attention_sees_new_token, {}),
+]
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _failing_pins(lib_path):
+    """Run the fast pins against a library build in a child process (a
+    mutant may also fault); returns the failing pin names, or ["crash"]."""
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from tests.test_oracle_mutants import _run_pins\n"
+        "print('FAILED=' + ','.join(_run_pins(%r)))\n" % (ROOT, lib_path)
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return ["crash"]
+    line = [x for x in r.stdout.splitlines() if x.startswith("FAILED=")][-1]
+    return [x for x in line[len("FAILED="):].split(",") if x]
+
+
+def _run_pins(lib_path):
+    orc = oracle_pkg.Oracle(lib_path)
+    failed = []
+    for fn, kw in FAST_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                fn(orc, **kw)
+        except (AssertionError, ValueError):
+            failed.append(fn.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle_pkg.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutant_src = tmp_path / "oracle_mutant.cpp"
+    mutant_src.write_text(src.replace(old, new))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    subprocess.run(["g++", *oracle_pkg.CXXFLAGS, str(mutant_src), "-o", lib], check=True)
+    failed = _failing_pins(lib)
+    assert failed, f"no pin caught mutant {name}"
+
+
+def test_unmutated_copy_passes_fast_pins(tmp_path):
+    lib = str(tmp_path / "liboracle_copy.so")
+    shutil.copy(oracle_pkg.SRC, tmp_path / "oracle_copy.cpp")
+    subprocess.run(["g++", *oracle_pkg.CXXFLAGS, str(tmp_path / "oracle_copy.cpp"), "-o", lib], check=True)
+    assert _failing_pins(lib) == []
