@@ -1,0 +1,234 @@
+"""Decode-attention throughput of libpagedattn on one MI355X.
+
+A step is one pass of the whole hot path over one batch: kv_append (the
+step's new K/V scattered into each row's last block) then paged_decode_attn
+(every row's blocks gathered at its own length, grouped-query attention for
+one query token), for every layer of the workload.
+
+Default workload: batch 32, Qwen2.5-1.5B attention shape (12 query heads,
+2 KV heads, head_dim 128, fp16), block 64, every row at length 1024, blocks
+shuffled over a 1024-block pool. Inputs are synthetic N(0,1) fp16 and
+resident in HBM before timing starts; R replicas of the pools (distinct
+memory, ~1 GiB touched in total) are rotated so consecutive steps stream
+from HBM rather than the 256 MB last-level cache.
+
+Output: one JSON line. `value` is algorithmic bytes moved per step (every
+row's K and V at its own length, q, out, table entries, lengths, and the
+append's reads and writes) divided by the measured time per step. The
+`roofline` object reports the decode kernel alone: its algorithmic bytes per
+launch over its average launch duration (HIP events around each launch on
+the launch stream), against 8 TB/s. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def decode_bytes(w: wl.Workload, unique=False) -> int:
+    kv = w.unique_kv_bytes_per_layer() if unique else w.kv_bytes_per_layer()
+    qo = 2 * w.B * w.Hq * w.D * 2
+    table = 4 * int(sum(wl.blocks_for(int(L), w.bs) for L in w.seq_lens))
+    return kv + qo + table + 4 * w.B
+
+
+def append_bytes(w: wl.Workload) -> int:
+    rows = int(np.sum(w.seq_lens >= 1))
+    return rows * w.Hkv * w.D * 2 * 2 * 2 + rows * 4 + 4 * w.B
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="uniform1024", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--replicas", type=int, default=0, help="pool replicas rotated per step (0 = auto, ~1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            f"bench.py measures one GPU only: the decode path has no cross-GPU step here "
+            f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_06_amd as pa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = wl.CONFIGS[args.config]()
+    layers = w.layers
+
+    # ---- inputs, resident on the device
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tables = dev(w.tables)
+    lens = dev(w.seq_lens)
+    touched = decode_bytes(w) * layers
+    R = args.replicas or (1 if layers > 1 else max(1, math.ceil((1 << 30) / touched)))
+    host0 = w.layer(0)
+    sets = []  # per replica: list over layers of (q, k_new, v_new, k_pool, v_pool)
+    for r in range(R):
+        per_layer = []
+        for layer in range(layers):
+            ld = host0 if layer == 0 else w.layer(layer)
+            if r == 0:
+                per_layer.append([dev(ld.q), dev(ld.k_new), dev(ld.v_new), dev(ld.k_pool), dev(ld.v_pool)])
+            else:
+                per_layer.append([t.clone() for t in sets[0][layer]])
+        sets.append(per_layer)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float16, device="cuda")
+    ws = pa.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.bs, w.W)
+    torch.cuda.synchronize()
+
+    def step(i):
+        for q, kn, vn, kp, vp in sets[i % R]:
+            pa.kv_append(kn, vn, kp, vp, tables, lens, w.bs)
+            pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
+
+    # ---- whole-step throughput
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-launch durations of each kernel (events around each launch)
+    n_k = max(20, min(args.steps, 400))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    for i in range(n_k):
+        q, kn, vn, kp, vp = sets[i % R][i % layers]
+        ev_a[i][0].record()
+        pa.kv_append(kn, vn, kp, vp, tables, lens, w.bs)
+        ev_a[i][1].record()
+        ev[i][0].record()
+        pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    app_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
+
+    step_bytes = (decode_bytes(w) + append_bytes(w)) * layers
+    unique_step_bytes = (decode_bytes(w, unique=True) + append_bytes(w)) * layers
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = decode_bytes(w) / (dec_ms * 1e-3) / 1e9
+    dec_unique_gbs = decode_bytes(w, unique=True) / (dec_ms * 1e-3) / 1e9
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        orc = oracle.get()
+        threads = min(16, os.cpu_count() or 1)
+        kp_h = sets[0][0][3].cpu().numpy()
+        vp_h = sets[0][0][4].cpu().numpy()
+        q_h, kn_h, vn_h = (sets[0][0][j].cpu().numpy() for j in range(3))
+        reps, t_used = 0, 0.0
+        start = time.perf_counter()
+        while True:
+            orc.kv_append(kn_h, vn_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs)
+            orc.paged_decode_attn(q_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs, w.scale, nthreads=threads)
+            reps += 1
+            t_used = time.perf_counter() - start
+            if t_used >= min(2.0, args.cpu_seconds) or reps * (t_used / reps) * (1 + 1 / reps) > args.cpu_seconds:
+                break
+        per_layer_s = t_used / reps
+        cpu = {
+            "value": round((decode_bytes(w) + append_bytes(w)) / per_layer_s / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} x (kv_append + paged_decode_attn) of layer 0 of the same workload "
+                      f"({w.B} rows), {threads} threads, {t_used:.2f} s",
+            "rows_layers_per_s": round(w.B / per_layer_s, 2),
+        }
+
+    cfg = {
+        "workload": w.name,
+        "batch": w.B,
+        "layers": layers,
+        "num_heads": w.Hq,
+        "num_kv_heads": w.Hkv,
+        "head_dim": w.D,
+        "block_size": w.bs,
+        "max_blocks_per_seq": w.W,
+        "pool_blocks": w.N,
+        "seq_len_min": int(w.seq_lens.min()),
+        "seq_len_max": int(w.seq_lens.max()),
+        "seq_len_sum": int(w.seq_lens.sum()),
+        "replicas": R,
+    }
+    line = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and rows*layers/s at batch 32",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": cfg,
+        "pct_of_peak": round(100 * unique_step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "rows_layers_per_s": round(w.B * layers / (ms_per_step * 1e-3), 1),
+        "bytes_per_step": step_bytes,
+        "unique_bytes_per_step": unique_step_bytes,
+        "decode_us": round(dec_ms * 1e3, 3),
+        "append_us": round(app_ms * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dec_unique_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_unique_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_kernel",
+            "bytes_per_launch": decode_bytes(w, unique=True),
+            "logical_GBs": round(dec_gbs, 2),
+        },
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * libpagedattn -- paged KV-cache decode attention for AMD Instinct MI355X
+ * (gfx950), behind a C ABI.
+ *
+ * Sources (page title, section):
+ *   [Paged attention]     danielfleming.xyz/writing/inference/paged
+ *   [PagedAttention]      deepconcepts.dev/c/llm-paged-attention
+ *   [SLM paged attention] aicassindra.com/blogs/slm/slm_paged_attention.html
+ *
+ * The problem. Keys and values of every sequence live in one preallocated
+ * pool cut into equal blocks of `block_size` tokens [SLM paged attention,
+ * "The architecture: every piece explained"]. Each sequence owns a block
+ * table: entry n is the physical block that holds its tokens
+ * n*block_size .. (n+1)*block_size-1 [PagedAttention, intro; SLM paged
+ * attention, same section]. A decode step appends the new token's K/V into
+ * the sequence's last block, a fresh block having been appended to the table
+ * by the host when the previous one filled [SLM paged attention, "End-to-end
+ * flow"], and then attends, for each sequence, over only the blocks its table
+ * lists, at its own true length [Paged attention, "What changed"]. The result
+ * is exact softmax attention; splitting the sum over blocks does not change
+ * it [PagedAttention, "Sharing is the part that pays twice"]. Several query
+ * heads share one KV head (grouped-query attention: 12 query heads over 2 KV
+ * heads for Qwen2.5-1.5B [Paged attention, "What a small pool does"]).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ *  - All data pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *    owned by the caller. The library allocates nothing and keeps no state
+ *    between calls except a per-device cache of the compute-unit count.
+ *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it and returns; there is no host synchronisation and
+ *    no device value is read on the host.
+ *  - Shapes (row-major, innermost last):
+ *      q, out         [B][Hq][D]
+ *      k_new, v_new   [B][Hkv][D]
+ *      k_pool         [N][Hkv][D/8][block_size][8]   (8 channels = 16 bytes,
+ *                                                     token-minor)
+ *      v_pool         [N][Hkv][D][block_size]        (tokens contiguous)
+ *      block_tables   [B][W] int32, W = max_blocks_per_seq
+ *      seq_lens       [B]    int32
+ *    B = num_seqs, Hq = num_heads, Hkv = num_kv_heads, D = head_dim,
+ *    N = num_blocks. Query head h reads KV head h / (Hq / Hkv).
+ *  - seq_lens[b] is the row's length INCLUDING the token of this step: the
+ *    append writes position seq_lens[b]-1 and attention covers positions
+ *    0 .. seq_lens[b]-1. A row with seq_lens[b] == 0 is skipped by
+ *    kv_append and gets zeros from paged_decode_attn.
+ *  - Table entries at index >= ceil(seq_lens[b] / block_size) are never
+ *    read and may hold anything (e.g. -1). Pool slots outside every row's
+ *    live range may hold anything, including NaN.
+ *  - Device-data preconditions (not checked on the host, since checking
+ *    would need a device read): live table entries lie in [0, N);
+ *    seq_lens[b] <= W * block_size; in kv_append no two rows target the
+ *    same slot and no row appends into a block another row also lists.
+ *    Violations give unspecified results but never an out-of-bounds access:
+ *    the kernels clamp block ids into [0, N) and lengths into [0, W*bs].
+ *
+ * Errors: every call returns PA_OK, or a status before anything is
+ * enqueued (PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE), or
+ * PA_ERR_HIP if the launch itself failed. pa_status_string() names them.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, misalignment */
+    PA_ERR_UNSUPPORTED = 2, /* (block_size, head_dim, Hq/Hkv) combination not compiled in */
+    PA_ERR_HIP = 3,         /* the kernel launch failed */
+    PA_ERR_WORKSPACE = 4    /* workspace null or smaller than paged_decode_workspace_size() */
+} pa_status;
+
+/* Static string naming a status. Never NULL. */
+const char *pa_status_string(int status);
+
+/* 1 if paged_decode_attn has a kernel for this shape, else 0.
+ * Compiled in: block_size in {16, 32, 64, 128}, head_dim in {64, 128},
+ * num_heads / num_kv_heads in {1, 2, 4, 6, 8}. */
+int paged_decode_supported(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size);
+
+/*
+ * kv_append -- write one decode step's new key and value of every row into
+ * the row's last block [SLM paged attention, "End-to-end flow": a sequence
+ * grows one block at a time, the host appending a fresh block from the free
+ * list when the current one fills; "The architecture: every piece
+ * explained": logical block index = position / block_size].
+ *
+ * For each row b with L = seq_lens[b] >= 1: pos = L-1,
+ * blk = block_tables[b][pos / block_size], slot = pos % block_size, and for
+ * every KV head g and channel d
+ *     K[blk][g][d/8][slot][d%8] = k_new[b][g][d]
+ *     V[blk][g][d][slot]        = v_new[b][g][d]
+ * A pure bit copy; no other pool byte changes. Rows whose target block id is
+ * outside [0, N) or whose L exceeds W*block_size are skipped.
+ * k_new, v_new: 16-byte aligned. Supported: head_dim % 8 == 0, any
+ * block_size >= 1 (block_size % 8 == 0 not required).
+ */
+pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                    const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    void *stream);
+
+/*
+ * Bytes of device workspace paged_decode_attn needs for these sizes: the
+ * per-(row, KV head) arrival counters of the split-sequence reduction and the
+ * fp32 partial results (max, sum, unnormalised output per query head) of up
+ * to ceil(ceil(W*block_size/64)/4) sequence partitions per (row, KV head).
+ * Returns 0 for invalid sizes.
+ */
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq);
+
+/*
+ * Zero a workspace with a device fill kernel (no memset, so it may be
+ * captured in a HIP graph). A workspace must be all-zero before its first
+ * paged_decode_attn call; every completed call leaves its counters at zero
+ * again, so one init per allocation suffices.
+ */
+pa_status paged_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_decode_attn -- one query token per row, grouped-query softmax
+ * attention over the row's own blocks at its true length [Paged attention,
+ * "What changed"; PagedAttention, "What the block table costs": read the
+ * table, resolve each logical block to a physical one, gather;
+ * PagedAttention, "Sharing is the part that pays twice": block-wise softmax
+ * rescaled and combined exactly].
+ *
+ *   out[b][h][:] = sum_t softmax_t(scale * q[b][h] . k_t) v_t,
+ *   t = 0 .. seq_lens[b]-1, k_t / v_t from block block_tables[b][t/bs],
+ *   slot t % bs, KV head h / (Hq/Hkv).
+ *
+ * fp32 accumulation, fp16 output (round to nearest even). Long rows are
+ * split into partitions whose partial (max, sum, output) are merged in
+ * partition order by the last partition to finish, so results are
+ * bit-identical from run to run.
+ * q, out, k_pool, v_pool: 16-byte aligned. workspace: at least
+ * paged_decode_workspace_size() bytes, 256-byte aligned, zeroed once by
+ * paged_decode_workspace_init() (or any zero fill) before first use. Calls
+ * that are in flight at the same time must use different workspaces.
+ * Unsupported shapes (see paged_decode_supported) return PA_ERR_UNSUPPORTED.
+ */
+pa_status paged_decode_attn(uint16_t *out, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                            const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * paged_gather_kv -- debug path that reads the same blocks the decode kernel
+ * reads and writes them out contiguously [Paged attention, "What changed":
+ * the block machinery was first checked through a path that reads the same
+ * blocks with the earlier dense kernel].
+ *   k_out[b][g][t][d] = K[block_tables[b][t/bs]][g][d/8][t%bs][d%8]
+ *   v_out[b][g][t][d] = V[block_tables[b][t/bs]][g][d][t%bs]
+ * for t < seq_lens[b]; k_out / v_out are [B][Hkv][W*block_size][D] and their
+ * positions t >= seq_lens[b] are left untouched.
+ */
+pa_status paged_gather_kv(uint16_t *k_out, uint16_t *v_out, const uint16_t *k_pool, const uint16_t *v_pool,
+                          const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t num_blocks, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,185 @@
+"""Python binding of libpagedattn (paged KV-cache decode attention, MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libpagedattn.so`` (built from ``csrc/pagedattn.hip`` by ``build.py``).
+torch is used for device memory and streams. There is no CPU fallback: if
+the library is missing, or a tensor is not on the GPU, the call raises.
+
+Names and argument order follow the C ABI in ``include/pagedattn.h``:
+
+  kv_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size)
+  paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size,
+                    scale, out=None, workspace=None)
+  paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size)
+  paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                              block_size, max_blocks_per_seq)
+
+Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK = 0
+_ERRORS = {1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_HIP", 4: "PA_ERR_WORKSPACE"}
+
+_lib = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg}: {_ERRORS.get(status, status)}")
+        self.status = status
+
+
+def lib():
+    """Load libpagedattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with paged_kv_cache_06_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.paged_decode_supported.argtypes = [i32] * 4
+    L.paged_decode_supported.restype = ctypes.c_int
+    L.kv_append.argtypes = [vp] * 6 + [i32] * 6 + [vp]
+    L.kv_append.restype = ctypes.c_int
+    L.paged_decode_workspace_size.argtypes = [i32] * 6
+    L.paged_decode_workspace_size.restype = sz
+    L.paged_decode_workspace_init.argtypes = [vp, sz, vp]
+    L.paged_decode_workspace_init.restype = ctypes.c_int
+    L.paged_decode_attn.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
+    L.paged_decode_attn.restype = ctypes.c_int
+    L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
+    L.paged_gather_kv.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != PA_OK:
+        raise PagedAttnError(status, what)
+
+
+def _dev(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _pool_dims(k_pool, v_pool, block_size):
+    N, Hkv, D8, bs, eight = k_pool.shape
+    if eight != 8 or bs != block_size:
+        raise ValueError(f"k_pool must be [N][Hkv][D/8][{block_size}][8], got {tuple(k_pool.shape)}")
+    D = D8 * 8
+    if tuple(v_pool.shape) != (N, Hkv, D, bs):
+        raise ValueError(f"v_pool must be {(N, Hkv, D, bs)}, got {tuple(v_pool.shape)}")
+    return N, Hkv, D
+
+
+def paged_decode_supported(num_heads, num_kv_heads, head_dim, block_size) -> bool:
+    return bool(lib().paged_decode_supported(num_heads, num_kv_heads, head_dim, block_size))
+
+
+def kv_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size, stream=None):
+    """Write k_new / v_new [B][Hkv][D] at position seq_lens[b]-1 of each row."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, W = block_tables.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be [B]")
+    st = lib().kv_append(
+        _dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hkv, D, block_size, W, N, _stream(stream),
+    )
+    _check(st, "kv_append")
+
+
+def paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq):
+    return int(lib().paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                 max_blocks_per_seq))
+
+
+def new_workspace(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, device="cuda"):
+    """A zeroed workspace (int8 tensor) of the size paged_decode_attn needs."""
+    n = paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    paged_decode_workspace_init(ws)
+    return ws
+
+
+def paged_decode_workspace_init(workspace, stream=None):
+    st = lib().paged_decode_workspace_init(_dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                           _stream(stream))
+    _check(st, "paged_decode_workspace_init")
+
+
+def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, out=None, workspace=None,
+                      stream=None):
+    """out [B][Hq][D] fp16 = softmax(scale q k^T) v over each row's own blocks."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+    st = lib().paged_decode_attn(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
+    )
+    _check(st, "paged_decode_attn")
+    return out
+
+
+def paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size, k_out=None, v_out=None, stream=None):
+    """Debug path: [B][Hkv][W*bs][D] copies of each row's tokens (positions
+    past seq_lens[b] are left as they were in k_out / v_out)."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, W = block_tables.shape
+    shape = (B, Hkv, W * block_size, D)
+    if k_out is None:
+        k_out = torch.zeros(shape, dtype=torch.float16, device=k_pool.device)
+    if v_out is None:
+        v_out = torch.zeros(shape, dtype=torch.float16, device=k_pool.device)
+    st = lib().paged_gather_kv(
+        _dev(k_out, "k_out", torch.float16, 4), _dev(v_out, "v_out", torch.float16, 4),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hkv, D, block_size, W, N, _stream(stream),
+    )
+    _check(st, "paged_gather_kv")
+    return k_out, v_out
