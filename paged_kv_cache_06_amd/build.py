@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libpagedattn.so")
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     # packed fp32 VALU forms are kept out of every kernel
