@@ -16,14 +16,27 @@ Output: one JSON line. `value` is algorithmic bytes moved per step (every
 row's K and V at its own length, q, out, table entries, lengths, and the
 append's reads and writes) divided by the measured time per step. The
 `roofline` object reports the decode kernel alone: its algorithmic bytes per
-launch over its average launch duration (HIP events around each launch on
-the launch stream), against 8 TB/s. `cpu_baseline` times the CPU oracle on a
+launch over its average duration, measured with HIP events on the launch
+stream around launches issued back to back (events bracketing each single
+launch add a few microseconds of their own; that figure is
+`decode_us_bracketed`), against 8 TB/s. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
+
+`roofline.traffic` is the decode kernel's HBM bytes per launch from two
+rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this same script with
+--copy-calibration, each scaled by what the counter reads for a plain device
+copy of known size in the same run. `--pmc-summary FETCH_DIR WRITE_DIR`
+turns those runs into profiles/decode_kernel_<workload>_traffic.txt; the
+figure is reported only while the kernel source still has the hash recorded
+there, else null.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -39,6 +52,105 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", "pagedattn.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_KERNEL = "decode_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_REPS = 10
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_kernel_{workload}_traffic.txt")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "-")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _counter_per_dispatch(run_dir: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter (summed over the
+    dimensions rocprofv3 reports it in)."""
+    per = {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per.setdefault(key, [r["Kernel_Name"], 0.0])
+            per[key][1] += float(r["Counter_Value"])
+    out = {}
+    for name, v in per.values():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _median_for(values: dict, needle: str, largest: int = 0):
+    """Median over the dispatches of one kernel; with `largest`, over its
+    `largest` biggest readings only (the calibration copies, not the small
+    host-device transfers the same copy kernel also serves)."""
+    got = sorted(v for name, vs in values.items() if needle in name for v in vs)
+    if largest:
+        got = got[-largest:]
+    if not got:
+        raise SystemExit(f"no dispatch of {needle} in the counter output")
+    return float(np.median(got)), len(got)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, command: str) -> str:
+    """Summarise two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into HBM bytes per decode launch, each counter scaled by its reading for a
+    plain copy of copy_bytes (which reads and writes copy_bytes once)."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    f_dec, n_f = _median_for(fetch, DECODE_KERNEL)
+    w_dec, n_w = _median_for(write, DECODE_KERNEL)
+    f_cpy, n_fc = _median_for(fetch, COPY_KERNEL, largest=COPY_REPS)
+    w_cpy, n_wc = _median_for(write, COPY_KERNEL, largest=COPY_REPS)
+    f_scale = copy_bytes / (f_cpy * 1024.0)
+    w_scale = copy_bytes / (w_cpy * 1024.0)
+    traffic = f_dec * 1024.0 * f_scale + w_dec * 1024.0 * w_scale
+    w = wl.CONFIGS[workload]()
+    algo = decode_bytes(w, unique=True)
+    lines = [
+        f"# decode_kernel HBM traffic, workload {workload}",
+        f"# command: {command}",
+        f"workload: {workload}",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"decode_fetch_kib_per_dispatch_median: {f_dec:.1f}  (dispatches: {n_f})",
+        f"decode_write_kib_per_dispatch_median: {w_dec:.1f}  (dispatches: {n_w})",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_kib_per_dispatch_median: {f_cpy:.1f}  (dispatches: {n_fc})",
+        f"copy_write_kib_per_dispatch_median: {w_cpy:.1f}  (dispatches: {n_wc})",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"traffic_bytes_per_launch: {int(round(traffic))}",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"traffic_over_algorithmic: {traffic / algo:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def decode_bytes(w: wl.Workload, unique=False) -> int:
@@ -62,11 +174,25 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas rotated per step (0 = auto, ~1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help=f"after the bench, run {COPY_REPS} plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
+    ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
+    ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        text = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.pmc_copy_mib << 20,
+                           args.pmc_command)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_file(args.config), "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(
@@ -141,12 +267,23 @@ def main():
     torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     app_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
+    # decode launches back to back on the same stream: the average gap between
+    # consecutive completions, i.e. the kernel's duration without launch gaps
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for i in range(n_k):
+        q, kn, vn, kp, vp = sets[i % R][i % layers]
+        pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
+    b1.record()
+    torch.cuda.synchronize()
+    dec_b2b_ms = b0.elapsed_time(b1) / n_k
 
     step_bytes = (decode_bytes(w) + append_bytes(w)) * layers
     unique_step_bytes = (decode_bytes(w, unique=True) + append_bytes(w)) * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = decode_bytes(w) / (dec_ms * 1e-3) / 1e9
-    dec_unique_gbs = decode_bytes(w, unique=True) / (dec_ms * 1e-3) / 1e9
+    dec_gbs = decode_bytes(w) / (dec_b2b_ms * 1e-3) / 1e9
+    dec_unique_gbs = decode_bytes(w, unique=True) / (dec_b2b_ms * 1e-3) / 1e9
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -165,7 +302,7 @@ def main():
             orc.paged_decode_attn(q_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs, w.scale, nthreads=threads)
             reps += 1
             t_used = time.perf_counter() - start
-            if t_used >= min(2.0, args.cpu_seconds) or reps * (t_used / reps) * (1 + 1 / reps) > args.cpu_seconds:
+            if t_used + t_used / reps > args.cpu_seconds:  # the next repetition would pass the bound
                 break
         per_layer_s = t_used / reps
         cpu = {
@@ -211,7 +348,8 @@ def main():
         "rows_layers_per_s": round(w.B * layers / (ms_per_step * 1e-3), 1),
         "bytes_per_step": step_bytes,
         "unique_bytes_per_step": unique_step_bytes,
-        "decode_us": round(dec_ms * 1e3, 3),
+        "decode_us": round(dec_b2b_ms * 1e3, 3),
+        "decode_us_bracketed": round(dec_ms * 1e3, 3),
         "append_us": round(app_ms * 1e3, 3),
         "roofline": {
             "bound": "hbm",
@@ -219,7 +357,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dec_unique_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": read_traffic(w.name),
             "kernel": "decode_kernel",
             "bytes_per_launch": decode_bytes(w, unique=True),
             "logical_GBs": round(dec_gbs, 2),
@@ -228,6 +366,14 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
