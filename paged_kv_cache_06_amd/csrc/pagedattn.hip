@@ -68,8 +68,6 @@
 namespace {
 
 constexpr int kLanes = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kLanes * kWaves;
 constexpr int kTile = 64;  // tokens per tile (one lane per token in QK)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -204,40 +202,8 @@ __device__ __forceinline__ void score_block(float (&a)[4][4], const unsigned (&q
         : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
 }
 
-__device__ __forceinline__ int clamp_block(int blk, int N) {
-    return (unsigned)blk < (unsigned)N ? blk : 0;
-}
-
-// Row order of the V loads: register jj of a lane whose token chunk is c
-// holds channel rows 8*(jj ^ vrow_twist(c)) + l/8. The twist is linear in c
-// with twist(7) = NJ/2, twist(2) = NJ/4, twist(1) = NJ/8, matching the
-// partners of the three butterfly steps (lane c^7 by row_half_mirror, c^2 and
-// c^1 by quad permutes).
-template <int NJ>
-__device__ __forceinline__ int vrow_twist(int c) {
-    static_assert(NJ == 8 || NJ == 16, "head_dim 64 or 128");
-    const int t1 = NJ / 8, t2 = NJ / 4, t4 = (NJ / 2) ^ (NJ / 4) ^ (NJ / 8);
-    return ((c & 1) ? t1 : 0) ^ ((c & 2) ? t2 : 0) ^ ((c & 4) ? t4 : 0);
-}
-
 // ---------------------------------------------------------------------------
-// work decomposition shared by all workgroups of one decode launch
-// ---------------------------------------------------------------------------
-
-// Relaxed agent-scope atomic accesses compile to plain global loads/stores
-// with the sc1 bit: coherent across the GPU's L2 slices without a cache
-// writeback or invalidate. The split-sequence partials travel this way.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-constexpr int kMaxSplit = 16;  // partitions per (row, KV head), hard cap
-
-// ---------------------------------------------------------------------------
-// decode kernel
+// memory helpers
 // ---------------------------------------------------------------------------
 
 // s_waitcnt immediate that waits until at most `n` vector-memory operations of
@@ -249,16 +215,29 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// s_waitcnt lgkmcnt(0) alone: this wave's LDS (and scalar) accesses are done.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// The same with a wave-uniform run-time count (a scalar branch tree over the
+// immediate forms). Counts above 63 wait for 63, which is stricter.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmem_range(int n) {
+    if constexpr (LO == HI) {
+        wait_vmem<LO>();
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n <= MID)
+            wait_vmem_range<LO, MID>(n);
+        else
+            wait_vmem_range<MID + 1, HI>(n);
+    }
+}
+__device__ __forceinline__ void wait_vmem_dyn(int n) { wait_vmem_range<0, 63>(n < 0 ? 0 : (n > 63 ? 63 : n)); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Workgroup barrier without a memory fence. Inside the tile loop the only
 // data shared between waves are tiles written by direct-to-LDS loads, whose
-// completion each wave establishes itself with wait_vmem before arriving; a
-// fenced __syncthreads would also wait for the next tile's loads, which must
-// stay in flight. The signal fences keep the compiler from moving LDS
+// completion each wave establishes itself with a vmcnt wait before arriving;
+// a fenced __syncthreads would also wait for the next tiles' loads, which
+// must stay in flight. The signal fences keep the compiler from moving LDS
 // accesses across the barrier.
 __device__ __forceinline__ void tile_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -266,215 +245,359 @@ __device__ __forceinline__ void tile_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One 16-byte load per lane from global memory straight into LDS: lane i's
-// bytes land at dst + 16*i (dst is wave-uniform).
-__device__ __forceinline__ void load16_to_lds(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0);
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<size_t>((lds_ptr)p));
 }
 
-// Work item of a workgroup: (row b, KV head g, partition p) straight from the
-// block index. Partition p covers tiles [p*chunk, (p+1)*chunk) of the row;
-// `chunk` and the partition count `parts` are fixed by the host from the
-// table width, so a workgroup knows its tiles without reading any length.
-// Partitions that start past the row's end exit at once.
-//
-// Each tile stream of the workgroup (a pair of waves, or one wave when the
-// group has an odd number of query heads) owns an LDS K buffer and an LDS V
-// buffer holding the 64-token tile it is computing on; both waves of a pair
-// read the shared copy, each for its half of the query heads. The next tile
-// is requested into registers at the top of an iteration, every wave loading
-// its half with 16-byte loads, and written into the LDS buffers at the bottom,
-// after the current tile is consumed:
-//   request tile i+1 -> barrier -> scores, softmax, PV on tile i -> barrier
-//   -> wait for tile i+1, write it to LDS
-// So a tile is always in flight while the previous one is computed, held in
-// the register file, whose capacity (not the LDS's) then bounds the bytes in
-// flight per compute unit. The first tile goes straight into LDS.
+// The tile loop's vector-memory instructions are all issued from inline
+// assembly, so that the wave itself knows exactly how many are in flight: the
+// waits for a tile are counted from that (vm_count in the kernel), and the
+// compiler, which cannot see these instructions, inserts no waits of its own
+// for them. (Vector-memory operations of a wave complete in issue order on
+// this architecture, loads and stores alike, so "at most n outstanding"
+// means "everything issued before the last n has completed".)
+
+// One 16-byte load per lane from global memory straight into LDS: lane i's
+// bytes land at dst + 16*i (dst wave-uniform, passed in M0). One wait state
+// separates the compiler's write of M0 from the load that reads it.
+__device__ __forceinline__ void dma16(const void* src, unsigned dst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+}
+// Device-coherent (sc1) stores of the split-sequence partials and plain
+// stores of the output.
+__device__ __forceinline__ void st_f32_sc1(float* p, float v) {
+    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_2f32_sc1(float* p, float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 v = {a, b};
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+// Device-coherent (sc1) loads of the partials for the merge: buffer loads
+// over one (row, KV head)'s partials, cache policy sc1 (the same coherence as
+// a relaxed agent-scope atomic load), 8 or 16 bytes per lane.
+constexpr int kCoherent = 16;                     // cache-policy bits: sc1
+constexpr int kRawBufferFormat = 0x00020000;      // dword3 of a raw 32-bit buffer resource
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
+    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
+}
+
+__device__ __forceinline__ int clamp_block(int blk, int N) {
+    return (unsigned)blk < (unsigned)N ? blk : 0;
+}
+
+// ---------------------------------------------------------------------------
+// decode kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxRows = 512;    // rows per launch (longer batches are split by the host)
+constexpr int kMaxParts = 64;    // partitions per (row, KV head)
+constexpr int kMaxPending = 128; // split partitions one workgroup may finish
+
+// Work decomposition. A row of length L has ceil(L/64) tiles of 64 tokens; a
+// partition ("unit") is up to C consecutive tiles of one (row, KV head); a
+// row has np = max(1, ceil(tiles/C)) partitions per KV head (one, with no
+// tiles, for L = 0). Every workgroup reads seq_lens at start and builds the
+// prefix count of units per row in LDS, so the unit list holds only real work
+// and is the same in every workgroup. Workgroup w then takes a consecutive
+// range of ceil(units/G) of them (G workgroups, a persistent grid sized to the
+// GPU).
+struct Unit {
+    int u;        // unit index; >= total means none
+    int k;        // ordinal of the unit within this workgroup
+    int b, g, p;  // row, KV head, partition
+    int np;       // partitions of this (row, KV head)
+    int L;        // row length
+    int t0, t1;   // tiles [t0, t1) of the row
+};
+
+// One step of the tile pipeline: a tile (or, for an empty row, none) of a unit.
+struct Pos {
+    Unit n;
+    int t;             // tile index within the row
+    int e0, e1, e2, e3;  // physical blocks of the tile (e1..e3 used when blocks are shorter than a tile)
+    __device__ bool valid(int total) const { return n.u < total; }
+    __device__ bool has_tile() const { return t < n.t1; }
+    __device__ bool first() const { return t == n.t0; }
+    __device__ bool last() const { return t + 1 >= n.t1; }
+};
+
+// Row of unit u: the last row whose prefix count is <= u, by two rounds of a
+// 64-lane search over the LDS prefix array pre[0..B].
+__device__ __forceinline__ int find_row(const int* pre, int B, int u, int lane) {
+    const int S = (B + 63) / 64;  // rows per first-round lane
+    const int i1 = min(lane * S, B);
+    const unsigned long long m1 = __ballot(pre[i1] <= u && lane * S <= B);
+    const int r1 = (64 - __clzll(m1) - 1) * S;  // highest lane whose start is <= u
+    const int i2 = min(r1 + lane, B);
+    const unsigned long long m2 = __ballot(lane < S && pre[i2] <= u);
+    return __builtin_amdgcn_readfirstlane(r1 + (64 - __clzll(m2) - 1));
+}
+
 template <int BS, int D, int NREP>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) decode_kernel(
+struct Cfg {
+    static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
+    static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
+    static constexpr int WPT = (NREP % 2 == 0) ? 2 : 1;   // waves per workgroup, sharing every tile
+    static constexpr int HPW = NREP / WPT;                 // query heads per wave
+    static constexpr int LPW = NJ / WPT;                   // load instructions per wave per K (or V) tile
+    static constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
+    static constexpr int TILE = kTile * D;                 // halves per K (or V) tile
+    static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
+    static constexpr int QI = (QC + 64 * WPT - 1) / (64 * WPT);  // q load instructions per wave
+    static constexpr int QBUF = QI * WPT * 64 * 8;         // halves per q buffer
+    static constexpr int THREADS = 64 * WPT;
+    static_assert(TPB <= 4, "block size of at least 16 tokens");
+    static_assert(NJ % WPT == 0, "load split");
+};
+
+// decode_kernel: persistent, one workgroup of WPT waves (two when the group's
+// query-head count is even, one otherwise) per slot. Both waves read every
+// tile, each for half of the group's query heads.
+//
+// Tile pipeline (step j computes tile position P_j; buffers alternate by j):
+//   prologue:  issue K(P0), V(P0)
+//   step j:    wait K(P_j) -> barrier A -> [j = 0: issue K(P1)] issue V(P_{j+1}) into the V buffer
+//              freed by step j-1 -> QK + softmax on K(P_j) -> wait V(P_j) ->
+//              barrier B -> issue K(P_{j+2}) into the K buffer just read ->
+//              PV on V(P_j) -> if P_j ends its unit, store the unit's result
+// so 1.5 tiles of loads are in flight during every compute phase, across unit
+// boundaries as well. The query of a unit is loaded into LDS with the K tile
+// of its first position.
+//
+// Layouts: the K tile in LDS is [NJ][64 tokens][8 ch] (lane = token for QK);
+// the V tile is [NJ row blocks][8 chunks][8 rows][8 tokens], loaded so that a
+// load instruction still covers eight whole 128-byte rows of V. PV uses lane =
+// channel: lane ch reads the 8 chunks of its channel's 64 tokens, odd row
+// blocks in the order c^1, which keeps every 16-lane phase of the LDS read on
+// distinct banks. The p vector of a head (fp16, 64 tokens) is broadcast from
+// LDS. A lane thus owns whole output channels: no cross-lane reduction of the
+// output at all.
+//
+// Results: a one-partition row writes fp16 output directly; otherwise the
+// partition writes (max, sum, unnormalised output) with coherent stores and is
+// listed; at exit the workgroup takes one arrival ticket per listed partition
+// and merges every (row, KV head) for which it was last, in partition order.
+template <int BS, int D, int NREP>
+__global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
-    int32_t* __restrict__ counters, float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int W,
-    int N, int chunk, int parts, float scale_log2) {
-    constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
-    constexpr int WPT = (NREP % 2 == 0) ? 2 : 1;   // waves sharing one tile, each with part of the heads
-    constexpr int HPW = NREP / WPT;                 // query heads per wave
-    constexpr int TS = kWaves / WPT;                // tile streams per workgroup
-    constexpr int LPW = NJ / WPT;                   // load instructions per wave per K (or V) tile
-    constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
-    constexpr int TILE = kTile * D;                 // halves per K (or V) tile
+    int32_t* __restrict__ counters, float* __restrict__ part_ml, float* __restrict__ part_acc, int B, int Hkv,
+    int W, int N, int C, int P, float scale_log2) {
+    using K = Cfg<BS, D, NREP>;
+    constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, LPW = K::LPW, TPB = K::TPB;
+    constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
     static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_kv[TS][2][TILE];
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[kWaves][HPW][kTile];
-    __shared__ float s_m[TS][NREP];
-    __shared__ float s_l[TS][NREP];
-    __shared__ float s_w[kMaxSplit][NREP];
-    __shared__ float s_pm[kMaxSplit][NREP];
-    __shared__ float s_pl[kMaxSplit][NREP];
-    __shared__ float s_den[NREP];
-    __shared__ int s_last;
-    // after the tile loop the tile buffers hold the per-stream partial outputs
-    float(*s_acc)[NREP][D] = reinterpret_cast<float(*)[NREP][D]>(&s_kv[0][0][0]);
-    static_assert(sizeof(float) * TS * NREP * D <= sizeof(uint16_t) * TS * 2 * TILE, "s_acc alias");
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[2][TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QBUF];
+    __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][kTile];
+    __shared__ int s_len[kMaxRows];
+    __shared__ int s_pre[kMaxRows + 1];
+    __shared__ int s_pend[kMaxPending];  // (row*Hkv + g) of split partitions finished here
+    __shared__ int s_pend_np[kMaxPending];
+    __shared__ int s_npend;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = uniform(tid >> 6);
-    const int stream = wave / WPT;        // which tiles this wave walks
-    const int wip = wave % WPT;           // position of the wave in its pair
-    const int h0 = wip * HPW;             // its first query head within the group
-    const int bg = blockIdx.x / parts;
-    const int p = blockIdx.x - bg * parts;
-    const int b = bg / Hkv, g = bg - b * Hkv;
+    const int wip = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in the workgroup
+    const int h0 = wip * HPW;                                   // its first query head within the group
     const int Hq = Hkv * NREP;
+    const int G = gridDim.x;
     const int cap = W * BS;
-    const int wtiles = (cap + kTile - 1) / kTile;
-    const int t_begin = p * chunk;
-    const int32_t* __restrict__ trow = tables + (size_t)b * W;
-    uint16_t* __restrict__ orow = out + ((size_t)b * Hq + (size_t)g * NREP) * D;
-    const u32x4* __restrict__ qv = reinterpret_cast<const u32x4*>(q + ((size_t)b * Hq + (size_t)g * NREP) * D);
-    const int c = lane & 7;        // token chunk of this lane in the V layout
-    const int drow = lane >> 3;    // channel row offset within each group of 8
-    uint16_t* kbuf = &s_kv[stream][0][0];
-    uint16_t* vbuf = &s_kv[stream][1][0];
+    const int drow = lane & 7, vc = lane >> 3;  // V load lane: row within a row block, token chunk
 
-    // table entries of a tile: the block of this lane's K token and of its V
-    // chunk. A block past the row's last block is replaced by the tile's first
-    // block (its values are masked), so no unlisted entry is ever used.
-    auto k_block = [&](int t) { return TPB == 1 ? (t * kTile) / BS : (t * kTile + lane) / BS; };
-    auto v_block = [&](int t) { return (t * kTile + 8 * c) / BS; };
-
-    // ---- one round trip: the row's length, the query, the first table entry
-    int tile0 = t_begin + stream;
-    int kent = 0, vent = 0;
-    if (tile0 < wtiles) {  // inside the table row; used only if the tile is live
-        kent = TPB == 1 ? uniform(trow[k_block(tile0)]) : trow[min(k_block(tile0), W - 1)];
-        if constexpr (TPB > 1) vent = trow[min(v_block(tile0), W - 1)];
+    // ---- unit list: lengths and the prefix count of units per row
+    for (int r = tid; r < B; r += THREADS) {
+        int L = seq_lens[r];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        s_len[r] = L;
     }
-    // this wave's query heads: pair p of head h at lane p % 16 (every row) of qr[h][p / 16]
-    constexpr int QR = NJ / 4;
-    unsigned qr[HPW][QR];
-    {
-        const unsigned* qw = reinterpret_cast<const unsigned*>(qv) + (size_t)h0 * (D / 2);
+    if (tid == 0) s_npend = 0;
+    __syncthreads();
+    if (wip == 0) {
+        // serial over 64-row chunks, a wave-wide inclusive scan within each
+        int carry = 0;
+        for (int r0 = 0; r0 < B; r0 += 64) {
+            const int r = r0 + lane;
+            int nu = 0;
+            if (r < B) {
+                const int nt = (s_len[r] + kTile - 1) / kTile;
+                nu = Hkv * max(1, (nt + C - 1) / C);
+            }
+            int x = nu;
 #pragma unroll
-        for (int h = 0; h < HPW; ++h)
-#pragma unroll
-            for (int i = 0; i < QR; ++i) qr[h][i] = qw[h * (D / 2) + 16 * i + (lane & 15)];
+            for (int s = 1; s < 64; s <<= 1) {
+                const int y = __shfl_up(x, s);
+                if (lane >= s) x += y;
+            }
+            if (r < B) s_pre[r + 1] = carry + x;
+            carry += __shfl(x, 63);
+        }
+        if (lane == 0) s_pre[0] = 0;
     }
-    int L = seq_lens[b];
-    L = uniform(L < 0 ? 0 : (L > cap ? cap : L));
-    const int ntiles = (L + kTile - 1) / kTile;
-    if (t_begin >= ntiles && !(L == 0 && p == 0)) return;  // partition past the row's end
-    if (L == 0) {
-        for (int o = tid; o < NREP * D; o += kThreads) orow[o] = 0;
-        return;
-    }
-    const int nblk = (L + BS - 1) / BS;
-    const int t_end = min(ntiles, t_begin + chunk);
-    const int np = (ntiles + chunk - 1) / chunk;  // live partitions of this row
-    const int n_iter = (t_end - t_begin + TS - 1) / TS;
+    __syncthreads();
+    const int total = __builtin_amdgcn_readfirstlane(s_pre[B]);
+    wait_vmem<0>();  // nothing of the prologue is left in flight: the count below starts at zero
+    int vm_count = 0;
 
-    auto fix_entries = [&](int t, int& ke, int& ve) {
+    // workgroup w takes the consecutive units [w*per, (w+1)*per): the
+    // partitions of one (row, KV head) mostly land in one workgroup's range,
+    // so a workgroup rarely has more than one merge to do at exit
+    const int per = (total + G - 1) / G;
+    auto unit_at = [&](int k) {
+        Unit n;
+        n.k = k;
+        n.u = k < per ? (int)blockIdx.x * per + k : total;
+        n.b = n.g = n.p = n.L = n.t0 = n.t1 = 0;
+        n.np = 1;
+        if (n.u < total) {
+            n.b = find_row(s_pre, B, n.u, lane);
+            n.L = __builtin_amdgcn_readfirstlane(s_len[n.b]);
+            const int nt = (n.L + kTile - 1) / kTile;
+            n.np = max(1, (nt + C - 1) / C);
+            const int r = n.u - __builtin_amdgcn_readfirstlane(s_pre[n.b]);
+            n.g = r / n.np;
+            n.p = r - n.g * n.np;
+            n.t0 = n.p * C;
+            n.t1 = min(nt, n.t0 + C);
+        }
+        return n;
+    };
+    // table entries of a position's tile (scalar loads; entries past the
+    // row's last block are replaced by the tile's first, whose data is masked)
+    auto load_entries = [&](Pos& s) {
+        s.e0 = s.e1 = s.e2 = s.e3 = 0;
+        if (!s.valid(total) || !s.has_tile()) return;
+        const int32_t* trow = tables + (size_t)s.n.b * W;
+        const int n0 = (s.t * kTile) / BS;
+        const int nblk = (s.n.L + BS - 1) / BS;
+        s.e0 = trow[n0];
         if constexpr (TPB > 1) {
-            const int first = (t * kTile) / BS;
-            if (k_block(t) >= nblk) ke = trow[first];
-            if (v_block(t) >= nblk) ve = trow[first];
+            s.e1 = trow[n0 + 1 < nblk ? n0 + 1 : n0];
+            if constexpr (TPB > 2) {
+                s.e2 = trow[n0 + 2 < nblk ? n0 + 2 : n0];
+                s.e3 = trow[n0 + 3 < nblk ? n0 + 3 : n0];
+            }
         }
     };
-    auto next_entries = [&](int t, int& ke, int& ve) {
+    auto first_pos = [&](int k) {
+        Pos s;
+        s.n = unit_at(k);
+        s.t = s.n.t0;
+        load_entries(s);
+        return s;
+    };
+    auto next_pos = [&](const Pos& s) {
+        if (!s.valid(total)) return s;
+        if (s.t + 1 < s.n.t1) {
+            Pos r = s;
+            r.t = s.t + 1;
+            load_entries(r);
+            return r;
+        }
+        return first_pos(s.n.k + 1);
+    };
+    auto entry_for = [&](const Pos& s, int idx) {  // idx = block of the tile (0..TPB-1), wave-divergent
         if constexpr (TPB == 1) {
-            ke = uniform(trow[k_block(t)]);
+            return s.e0;
+        } else if constexpr (TPB == 2) {
+            return idx == 0 ? s.e0 : s.e1;
         } else {
-            const int first = (t * kTile) / BS;
-            ke = trow[k_block(t) < nblk ? k_block(t) : first];
-            ve = trow[v_block(t) < nblk ? v_block(t) : first];
+            return idx == 0 ? s.e0 : (idx == 1 ? s.e1 : (idx == 2 ? s.e2 : s.e3));
         }
     };
-    // This wave's half of a tile's 16-byte loads, straight into LDS.
-    auto issue_k = [&](int t, int ent) {
-        const int phys = clamp_block(ent, N);
-        const uint16_t* src = k_pool + ((size_t)phys * Hkv + g) * (size_t)(D * BS) +
-                              (size_t)((t * kTile + lane) % BS) * 8;
+
+    // ---- loads into LDS (this wave's share of each)
+    auto issue_q = [&](const Pos& s) {
+        const uint16_t* qrow = q + ((size_t)s.n.b * Hq + (size_t)s.n.g * NREP) * D;
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+            const int c = (i * WPT + wip) * 64 + lane;
+            dma16(qrow + 8 * min(c, QC - 1), lds_addr(&s_q[s.n.k & 1][(i * WPT + wip) * 512]));
+        }
+        vm_count += QI;
+    };
+    auto issue_k = [&](const Pos& s, int buf) {
+        const int tok = s.t * kTile + lane;
+        const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : lane / BS), N);
+        const uint16_t* src = k_pool + ((size_t)phys * Hkv + s.n.g) * (size_t)(D * BS) + (size_t)(tok % BS) * 8;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int j = i * WPT + wip;
-            load16_to_lds(src + (size_t)j * (BS * 8), kbuf + j * (kTile * 8));
+            dma16(src + (size_t)j * (BS * 8), lds_addr(&s_k[buf][j * 512]));
         }
+        vm_count += LPW;
     };
-    auto issue_v = [&](int t, int ent) {
-        const int phys = clamp_block(ent, N);
-        const uint16_t* src = v_pool + ((size_t)phys * Hkv + g) * (size_t)(D * BS) +
-                              (size_t)(drow * BS + (t * kTile + 8 * c) % BS);
+    auto issue_v = [&](const Pos& s, int buf) {
+        const int tok = s.t * kTile + 8 * vc;
+        const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (8 * vc) / BS), N);
+        const uint16_t* src =
+            v_pool + ((size_t)phys * Hkv + s.n.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS);
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int jj = i * WPT + wip;
-            load16_to_lds(src + (size_t)jj * (8 * BS), vbuf + jj * (kTile * 8));
+            dma16(src + (size_t)jj * (8 * BS), lds_addr(&s_v[buf][jj * 512]));
         }
+        vm_count += LPW;
     };
 
+    // ---- per-unit state
+    constexpr int QR = NJ / 4;
+    unsigned qr[HPW][QR];
+    float m[HPW], lsum[HPW], acc[HPW][NH];
 
-    float m[HPW], lsum[HPW], acc[HPW][NJ];
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-        m[h] = -INFINITY;
-        lsum[h] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[h][j] = 0.f;
+    Pos P0 = first_pos(0);
+    Pos P1 = next_pos(P0);
+    Pos P2 = next_pos(P1);
+    int mk0 = 0, mk1 = 0, mv0 = 0, mv1 = 0;  // vm_count after each buffer's last load
+    if (P0.valid(total) && P0.has_tile()) {
+        issue_q(P0);
+        issue_k(P0, 0);
+        mk0 = vm_count;
+        issue_v(P0, 0);
+        mv0 = vm_count;
     }
 
-    // The query registers must have landed before any tile load is in flight,
-    // so the compiler never has to wait for those loads to read them.
-    wait_vmem<0>();
-    if (tile0 < t_end) {
-        fix_entries(tile0, kent, vent);
-        issue_k(tile0, kent);
-        issue_v(tile0, TPB == 1 ? kent : vent);
-    }
-    // entries of the next tile of this stream
-    int kent_n = 0, vent_n = 0;
-    if (tile0 + TS < t_end) next_entries(tile0 + TS, kent_n, vent_n);
-
-    for (int it = 0; it < n_iter; ++it) {
-        const int tile = tile0 + it * TS;
-        const int t0 = tile * kTile;
-        const bool act = tile < t_end;             // this stream has a tile in this round
-        const bool more = tile + TS < t_end;       // ... and another after it
-        if (it == 0) {
-            wait_vmem<0>();                        // the first tile, loaded straight into LDS
-        } else {
-            wait_lds();  // this wave's LDS writes of the tile
-        }
-        // ---- request the next tile into registers (this wave's half of its loads)
-        u32x4 kst[LPW], vst[LPW];
-        if (more) {
-            const int nt = tile + TS;
-            const int kphys = clamp_block(kent_n, N);
-            const int vphys = clamp_block(TPB == 1 ? kent_n : vent_n, N);
-            const uint16_t* ksrc = k_pool + ((size_t)(TPB == 1 ? uniform(kphys) : kphys) * Hkv + g) * (size_t)(D * BS) +
-                                   (size_t)((nt * kTile + lane) % BS) * 8;
-            const uint16_t* vsrc = v_pool + ((size_t)(TPB == 1 ? uniform(vphys) : vphys) * Hkv + g) * (size_t)(D * BS) +
-                                   (size_t)(drow * BS + (nt * kTile + 8 * c) % BS);
-#pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                const int j = i * WPT + wip;
-                kst[i] = *reinterpret_cast<const u32x4*>(ksrc + (size_t)j * (BS * 8));
+    for (int j = 0; P0.valid(total); ++j) {
+        const int buf = j & 1;
+        const bool tile = P0.has_tile();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
+        tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
+        if (P1.valid(total) && P1.has_tile()) {
+            if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
+                if (P1.first()) issue_q(P1);
+                issue_k(P1, 1);
+                mk1 = vm_count;
             }
-#pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                const int jj = i * WPT + wip;
-                vst[i] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)jj * (8 * BS));
-            }
-            if (tile + 2 * TS < t_end) next_entries(tile + 2 * TS, kent_n, vent_n);
+            issue_v(P1, buf ^ 1);
+            if (buf) mv0 = vm_count; else mv1 = vm_count;
         }
-        tile_barrier();  // tile i is in LDS for both waves of every pair
-
-        if (act) {
+        if (tile) {
+            if (P0.first()) {
+                const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.n.k & 1][0]) + h0 * (D / 2);
+#pragma unroll
+                for (int h = 0; h < HPW; ++h)
+#pragma unroll
+                    for (int i = 0; i < QR; ++i) qr[h][i] = qw[h * (D / 2) + 16 * i + (lane & 15)];
+#pragma unroll
+                for (int h = 0; h < HPW; ++h) {
+                    m[h] = -INFINITY;
+                    lsum[h] = 0.f;
+#pragma unroll
+                    for (int c = 0; c < NH; ++c) acc[h][c] = 0.f;
+                }
+            }
             // ---- scores: lane = token, query pairs broadcast across lanes by DPP
-            float s[HPW];
+            const int t0 = P0.t * kTile;
             u32x4 kj[NJ];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) kj[j] = *reinterpret_cast<const u32x4*>(kbuf + j * (kTile * 8) + lane * 8);
+            for (int jj = 0; jj < NJ; ++jj) kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][jj * 512 + lane * 8]);
             float a4[4][HPW];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -488,175 +611,204 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
                     score_block<4 * (J % 4)>(a4, qj, kj[J]);
                 }(), ...);
             }(std::make_integer_sequence<int, NJ>{});
+            const bool live = t0 + lane < P0.n.L;
+            float s[HPW];
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) s[h] = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
-            const bool live = t0 + lane < L;
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) s[h] = live ? s[h] * scale_log2 : -INFINITY;
-            // ---- online softmax
+            for (int h = 0; h < HPW; ++h) {
+                s[h] = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
+                s[h] = live ? s[h] * scale_log2 : -INFINITY;
+            }
+            // ---- online softmax (exp2 domain)
             float alpha[HPW];
             bool rescale = false;
 #pragma unroll
             for (int h = 0; h < HPW; ++h) {
-                const float mt = wave_max(s[h]);
-                const float mn = fmaxf(m[h], mt);
+                const float mn = fmaxf(m[h], wave_max(s[h]));
                 alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
                 rescale |= alpha[h] != 1.0f;
                 m[h] = mn;
                 const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[h] - mn);
                 lsum[h] = lsum[h] * alpha[h] + (float)ph;
-                s_p[wave][h][lane] = ph;
+                s_p[wip][h][lane] = ph;
             }
             if (__builtin_amdgcn_readfirstlane((int)rescale)) {
 #pragma unroll
                 for (int h = 0; h < HPW; ++h)
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[h][j] *= alpha[h];
-            }
-            __builtin_amdgcn_wave_barrier();
-            // ---- PV: p of this lane's 8 tokens, V of its 8 tokens and channel rows
-            u32x4 mask = {~0u, ~0u, ~0u, ~0u};
-            if (t0 + kTile > L) {  // tokens past the row's end may hold NaN
-                const int n = L - (t0 + 8 * c);
-                mask.x = (n > 0 ? 0xffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-                mask.y = (n > 2 ? 0xffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
-                mask.z = (n > 4 ? 0xffffu : 0u) | (n > 5 ? 0xffff0000u : 0u);
-                mask.w = (n > 6 ? 0xffffu : 0u) | (n > 7 ? 0xffff0000u : 0u);
-            }
-            u32x4 pp[HPW];
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) pp[h] = *reinterpret_cast<const u32x4*>(&s_p[wave][h][8 * c]);
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) {
-                const u32x4 vj = *reinterpret_cast<const u32x4*>(vbuf + jj * (kTile * 8) + lane * 8) & mask;
-#pragma unroll
-                for (int h = 0; h < HPW; ++h) acc[h][jj] = dot8(pp[h], vj, acc[h][jj]);
+                    for (int c = 0; c < NH; ++c) acc[h][c] *= alpha[h];
             }
         }
-        tile_barrier();  // every wave is done reading tile i
-        if (more) {
-            // ---- tile i+1 into the LDS buffers (the compiler waits for the loads)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
+        tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
+        if (P2.valid(total) && P2.has_tile()) {
+            if (P2.first()) issue_q(P2);
+            issue_k(P2, buf);
+            if (buf) mk1 = vm_count; else mk0 = vm_count;
+        }
+        if (tile) {
+            // ---- PV: lane = channel; chunk c of the tile read in the order c ^ par
+            const int t0 = P0.t * kTile;
+            const int par = vc & 1;  // parity of this lane's row block (lane / 8)
+            const uint16_t* vb = &s_v[buf][(lane >> 3) * 512 + drow * 8];
+            const _Float16* pb = &s_p[wip][0][0];
+            // every LDS read of the phase first (one latency), then the dot products
+            u32x4 pv[8][HPW], vv[8][NH];
 #pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                const int j = i * WPT + wip;
-                *reinterpret_cast<u32x4*>(kbuf + j * (kTile * 8) + lane * 8) = kst[i];
-                *reinterpret_cast<u32x4*>(vbuf + j * (kTile * 8) + lane * 8) = vst[i];
+            for (int c = 0; c < 8; ++c) {
+                const int cc = c ^ par;  // the chunk this lane reads at step c
+#pragma unroll
+                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * kTile + 8 * cc);
+#pragma unroll
+                for (int hv = 0; hv < NH; ++hv) vv[c][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8 * 512 + cc * 64);
+            }
+            if (t0 + kTile > P0.n.L) {  // tokens past the row's end may hold NaN: zero their V
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int n = P0.n.L - (t0 + 8 * (c ^ par));
+                    u32x4 mask;
+                    mask.x = (n > 0 ? 0xffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
+                    mask.y = (n > 2 ? 0xffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
+                    mask.z = (n > 4 ? 0xffffu : 0u) | (n > 5 ? 0xffff0000u : 0u);
+                    mask.w = (n > 6 ? 0xffffu : 0u) | (n > 7 ? 0xffff0000u : 0u);
+#pragma unroll
+                    for (int hv = 0; hv < NH; ++hv) vv[c][hv] &= mask;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int hv = 0; hv < NH; ++hv)
+#pragma unroll
+                    for (int h = 0; h < HPW; ++h) acc[h][hv] = dot8(pv[c][h], vv[c][hv], acc[h][hv]);
+        }
+        if (P0.last()) {
+            // ---- the unit's result
+            const int b = P0.n.b, g = P0.n.g;
+            float lt[HPW];
+#pragma unroll
+            for (int h = 0; h < HPW; ++h) lt[h] = tile ? wave_sum(lsum[h]) : 1.f;
+            if (P0.n.np == 1) {
+                uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + h0) * D + lane;
+#pragma unroll
+                for (int h = 0; h < HPW; ++h)
+#pragma unroll
+                    for (int hv = 0; hv < NH; ++hv) {
+                        const float o = tile ? acc[h][hv] / lt[h] : 0.f;
+                        st_u16(orow + h * D + hv * 64, __builtin_bit_cast(uint16_t, (_Float16)o));
+                    }
+                vm_count += HPW * NH;
+            } else {
+                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.n.p) * NREP + h0;
+                float* pa = part_acc + slot * D + lane;
+#pragma unroll
+                for (int h = 0; h < HPW; ++h)
+#pragma unroll
+                    for (int hv = 0; hv < NH; ++hv) st_f32_sc1(pa + h * D + hv * 64, acc[h][hv]);
+                float* pm = part_ml + slot * 2;
+                if (lane == 0) {
+#pragma unroll
+                    for (int h = 0; h < HPW; ++h) st_2f32_sc1(pm + 2 * h, m[h], lt[h]);
+                }
+                vm_count += HPW * NH + HPW;
+                if (wip == 0 && lane == 0) {
+                    const int n = s_npend;
+                    if (n < kMaxPending) {
+                        s_pend[n] = b * Hkv + g;
+                        s_pend_np[n] = P0.n.np;
+                        s_npend = n + 1;
+                    }
+                }
             }
         }
+        P0 = P1;
+        P1 = P2;
+        P2 = next_pos(P2);
     }
 
-    // ---- per-wave epilogue: l over all lanes, acc over the 8 lanes of a channel row
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-        lsum[h] = wave_sum(lsum[h]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            float x = acc[h][j];
-            x += dpp<kQuadXor1>(x);
-            x += dpp<kQuadXor2>(x);
-            x += dpp<kHalfMirror>(x);
-            acc[h][j] = x;
-        }
-    }
-    // (the last loop barrier guarantees the tile buffers are no longer read)
-    if (c == 0) {
-#pragma unroll
-        for (int h = 0; h < HPW; ++h)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) s_acc[stream][h0 + h][8 * j + drow] = acc[h][j];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < HPW; ++h) {
-            s_m[stream][h0 + h] = m[h];
-            s_l[stream][h0 + h] = lsum[h];
-        }
+    // ---- tickets and merges of split (row, KV head)s
+    __builtin_amdgcn_s_waitcnt(0);  // every partial of this workgroup is stored
+    __syncthreads();
+    const int npend = __builtin_amdgcn_readfirstlane(s_npend);
+    for (int e = tid; e < npend; e += THREADS) {
+        const int t = __hip_atomic_fetch_add(&counters[s_pend[e]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_pend_np[e] = (t == s_pend_np[e] - 1) ? s_pend_np[e] : -s_pend_np[e];  // > 0: this workgroup merges
     }
     __syncthreads();
-
-    // ---- merge the tile streams of this workgroup
-    const bool single = np == 1;
-    float* pacc = part_acc + ((size_t)bg * parts + p) * (size_t)(NREP * D);
-    float* pml = part_ml + ((size_t)bg * parts + p) * (size_t)(NREP * 2);
-    for (int o = tid; o < NREP * D; o += kThreads) {
-        const int h = o / D, d = o % D;
-        float M = s_m[0][h];
+    // Merge: every thread owns 4-channel chunks of the group's output and
+    // combines the partitions in partition order, eight at a time with all
+    // their loads in flight together (running max, rescaled sums).
+    constexpr int NC4 = NREP * D / 4;
+    constexpr int CPT = (NC4 + THREADS - 1) / THREADS;  // chunks per thread
+    constexpr int MB = 8;                               // partitions per round trip
+    for (int e = 0; e < npend; ++e) {
+        const int np = __builtin_amdgcn_readfirstlane(s_pend_np[e]);
+        if (np <= 0) continue;
+        const int bg = __builtin_amdgcn_readfirstlane(s_pend[e]);
+        const float* ml0 = part_ml + (size_t)bg * P * NREP * 2;
+        const float* acc0 = part_acc + (size_t)bg * P * NREP * D;
+        const __amdgpu_buffer_rsrc_t rml =
+            __builtin_amdgcn_make_buffer_rsrc((void*)ml0, 0, np * NREP * 2 * 4, kRawBufferFormat);
+        const __amdgpu_buffer_rsrc_t racc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)acc0, 0, np * NREP * D * 4, kRawBufferFormat);
+        uint16_t* orow = out + (size_t)bg * NREP * D;  // (b*Hq + g*NREP)*D with bg = b*Hkv + g
+        float M[CPT], den[CPT];
+        f32x4 num[CPT];
 #pragma unroll
-        for (int w = 1; w < TS; ++w) M = fmaxf(M, s_m[w][h]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < TS; ++w) {
-            const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-            num += f * s_acc[w][h][d];
-            den += f * s_l[w][h];
+        for (int i = 0; i < CPT; ++i) {
+            M[i] = -INFINITY;
+            den[i] = 0.f;
+            num[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (single) {
-            orow[o] = __builtin_bit_cast(uint16_t, (_Float16)(num / den));
-        } else {
-            store_coherent(pacc + o, num);
-            if (d == 0) {
-                store_coherent(pml + 2 * h, M);
-                store_coherent(pml + 2 * h + 1, den);
+        for (int p0 = 0; p0 < np; p0 += MB) {
+            float mv[CPT][MB], lv[CPT][MB];
+            f32x4 av[CPT][MB];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c4 = min(tid + i * THREADS, NC4 - 1);
+                const int h = (4 * c4) / D;
+#pragma unroll
+                for (int k = 0; k < MB; ++k) {
+                    const int pp = min(p0 + k, np - 1);  // past np: a repeat, weighted 0 below
+                    const f32x2 ml = __builtin_bit_cast(
+                        f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, (pp * NREP + h) * 8, 0, kCoherent));
+                    mv[i][k] = ml.x;
+                    lv[i][k] = ml.y;
+                    av[i][k] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(racc, (pp * NREP * D + 4 * c4) * 4, 0, kCoherent));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                float mb = M[i];
+#pragma unroll
+                for (int k = 0; k < MB; ++k)
+                    if (p0 + k < np) mb = fmaxf(mb, mv[i][k]);
+                const float r = __builtin_amdgcn_exp2f(M[i] - mb);  // 0 on the first batch (M = -inf)
+                den[i] *= r;
+                num[i] *= r;
+#pragma unroll
+                for (int k = 0; k < MB; ++k) {
+                    const float w = (p0 + k < np) ? __builtin_amdgcn_exp2f(mv[i][k] - mb) : 0.f;
+                    den[i] += w * lv[i][k];
+                    num[i] += w * av[i][k];
+                }
+                M[i] = mb;
             }
         }
-    }
-    if (single) return;
-
-    // ---- split-sequence reduction: the last partition to arrive merges all
-    // partitions in partition order. Partials were written coherently; the
-    // wait makes them complete before this workgroup's ticket is taken.
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(&counters[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const float* acc0 = part_acc + (size_t)bg * parts * (size_t)(NREP * D);
-    const float* ml0 = part_ml + (size_t)bg * parts * (size_t)(NREP * 2);
-    // every partial is requested at once: one round trip, not one per partition
-    for (int e = tid; e < np * NREP; e += kThreads) {
-        const int pp = e / NREP, h = e - pp * NREP;
-        s_pm[pp][h] = load_coherent(ml0 + pp * NREP * 2 + 2 * h);
-        s_pl[pp][h] = load_coherent(ml0 + pp * NREP * 2 + 2 * h + 1);
-    }
-    constexpr int OPT = (NREP * D + kThreads - 1) / kThreads;  // outputs per thread
-    float part[OPT][kMaxSplit];
 #pragma unroll
-    for (int i = 0; i < OPT; ++i) {
-        const int o = tid + i * kThreads;
-        const int oc = o < NREP * D ? o : 0;
-#pragma unroll
-        for (int pp = 0; pp < kMaxSplit; ++pp)  // partitions past np re-read the last one (unused)
-            part[i][pp] = load_coherent(acc0 + (pp < np ? pp : np - 1) * NREP * D + oc);
-    }
-    __syncthreads();
-    if (tid < NREP) {
-        const int h = tid;
-        float M = -INFINITY;
-        for (int pp = 0; pp < np; ++pp) M = fmaxf(M, s_pm[pp][h]);
-        float den = 0.f;
-        for (int pp = 0; pp < np; ++pp) {
-            const float f = __builtin_amdgcn_exp2f(s_pm[pp][h] - M);
-            s_w[pp][h] = f;
-            den += f * s_pl[pp][h];
+        for (int i = 0; i < CPT; ++i) {
+            const int c4 = tid + i * THREADS;
+            if (c4 < NC4) {
+                const f32x4 o = num[i] / den[i];
+                typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                const f16x4 oh = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
+                *reinterpret_cast<f16x4*>(orow + 4 * c4) = oh;
+            }
         }
-        s_den[h] = den;
+        if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < OPT; ++i) {
-        const int o = tid + i * kThreads;
-        if (o >= NREP * D) break;
-        const int h = o / D;
-        float num = 0.f;
-#pragma unroll
-        for (int pp = 0; pp < kMaxSplit; ++pp)
-            if (pp < np) num += s_w[pp][h] * part[i][pp];
-        orow[o] = __builtin_bit_cast(uint16_t, (_Float16)(num / s_den[h]));
-    }
-    if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -724,18 +876,26 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
 // host side
 // ---------------------------------------------------------------------------
 
-typedef void (*DecodeFn)(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
-                         const int32_t*, int32_t*, float*, float*, int, int, int, int, int, float);
+struct DecodeFn {
+    const void* fn;
+    int threads;
+    explicit operator bool() const { return fn != nullptr; }
+};
+
+template <int BS, int D, int NREP>
+DecodeFn make_fn() {
+    return {reinterpret_cast<const void*>(decode_kernel<BS, D, NREP>), Cfg<BS, D, NREP>::THREADS};
+}
 
 template <int BS, int D>
 DecodeFn pick_nrep(int nrep) {
     switch (nrep) {
-        case 1: return decode_kernel<BS, D, 1>;
-        case 2: return decode_kernel<BS, D, 2>;
-        case 4: return decode_kernel<BS, D, 4>;
-        case 6: return decode_kernel<BS, D, 6>;
-        case 8: return decode_kernel<BS, D, 8>;
-        default: return nullptr;
+        case 1: return make_fn<BS, D, 1>();
+        case 2: return make_fn<BS, D, 2>();
+        case 4: return make_fn<BS, D, 4>();
+        case 6: return make_fn<BS, D, 6>();
+        case 8: return make_fn<BS, D, 8>();
+        default: return {nullptr, 0};
     }
 }
 
@@ -744,7 +904,7 @@ DecodeFn pick_d(int D, int nrep) {
     switch (D) {
         case 64: return pick_nrep<BS, 64>(nrep);
         case 128: return pick_nrep<BS, 128>(nrep);
-        default: return nullptr;
+        default: return {nullptr, 0};
     }
 }
 
@@ -754,18 +914,32 @@ DecodeFn pick_decode(int bs, int D, int nrep) {
         case 32: return pick_d<32>(D, nrep);
         case 64: return pick_d<64>(D, nrep);
         case 128: return pick_d<128>(D, nrep);
-        default: return nullptr;
+        default: return {nullptr, 0};
     }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Partitions per (row, KV head) the workspace must hold: a partition has at
-// least two tiles (one per tile stream of a workgroup) and there are never
-// more than kMaxSplit of them.
-int max_parts_for(int bs, int W) {
-    const long long tiles = ((long long)W * bs + kTile - 1) / kTile;
-    return (int)std::min<long long>(kMaxSplit, (tiles + 1) / 2);
+// Partition plan, fixed on the host from sizes alone (no device value is
+// read): C tiles per partition, so that a batch whose rows all fill the
+// table width gives about 1024 partitions (several per workgroup slot of
+// the GPU, for balance), with at most kMaxParts partitions per row.
+struct Plan {
+    long long wtiles;  // tiles of a full-width row
+    int rows;          // rows per launch
+    int C;             // tiles per partition
+    int P;             // partitions per (row, KV head), at most
+};
+
+Plan make_plan(int B, int Hkv, int bs, int W) {
+    Plan pl;
+    pl.wtiles = ((long long)W * bs + kTile - 1) / kTile;
+    pl.rows = std::max(1, std::min(B, kMaxRows));
+    const long long work = (long long)pl.rows * Hkv * pl.wtiles;
+    const long long c = std::max((pl.wtiles + kMaxParts - 1) / kMaxParts, (work + 1023) / 1024);
+    pl.C = (int)std::max(1LL, std::min(c, pl.wtiles));
+    pl.P = (int)((pl.wtiles + pl.C - 1) / pl.C);
+    return pl;
 }
 
 size_t counters_bytes(int B, int Hkv) { return (((size_t)B * Hkv * 4) + 255) / 256 * 256; }
@@ -782,6 +956,30 @@ int cu_count() {
         g_cu_count[dev].store(n, std::memory_order_relaxed);
     }
     return n;
+}
+
+// Resident workgroups per compute unit for a decode kernel (cached per
+// device and kernel; the kernel set is small and fixed).
+int blocks_per_cu(const DecodeFn& f) {
+    struct Entry {
+        std::atomic<const void*> fn;
+        std::atomic<int> dev, occ;
+    };
+    static Entry cache[256];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const size_t h = (reinterpret_cast<uintptr_t>(f.fn) / 16 + (size_t)dev * 31) % 256;
+    Entry& e = cache[h];
+    if (e.fn.load(std::memory_order_acquire) == f.fn && e.dev.load(std::memory_order_relaxed) == dev) {
+        const int o = e.occ.load(std::memory_order_relaxed);
+        if (o > 0) return o;
+    }
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f.fn, f.threads, 0) != hipSuccess || occ <= 0) occ = 1;
+    e.occ.store(occ, std::memory_order_relaxed);
+    e.dev.store(dev, std::memory_order_relaxed);
+    e.fn.store(f.fn, std::memory_order_release);
+    return occ;
 }
 
 }  // namespace
@@ -801,7 +999,7 @@ const char* pa_status_string(int status) {
 
 int paged_decode_supported(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
     if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads) return 0;
-    return pick_decode(block_size, head_dim, num_heads / num_kv_heads) != nullptr;
+    return pick_decode(block_size, head_dim, num_heads / num_kv_heads).fn != nullptr;
 }
 
 pa_status kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
@@ -827,9 +1025,9 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0)
         return 0;
-    const size_t parts = (size_t)max_parts_for(block_size, max_blocks_per_seq);
     const size_t rows = (size_t)(num_seqs > 0 ? num_seqs : 1);
-    return counters_bytes((int)rows, num_kv_heads) + rows * parts * (size_t)num_heads * (head_dim + 2) * 4;
+    const Plan pl = make_plan((int)rows, num_kv_heads, block_size, max_blocks_per_seq);
+    return counters_bytes((int)rows, num_kv_heads) + rows * (size_t)pl.P * num_heads * (head_dim + 2) * 4;
 }
 
 pa_status paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -860,36 +1058,35 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
                                                     max_blocks_per_seq);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return PA_ERR_WORKSPACE;
-    // Partition plan, fixed from the table width: tiles of 64 tokens, `chunk`
-    // tiles per partition (a multiple of the workgroup's tile streams), sized
-    // so that B*Hkv*parts workgroups give about two per compute unit, with at
-    // most kMaxSplit partitions per row.
-    const int ts = (nrep % 2 == 0) ? kWaves / 2 : kWaves;
-    const long long wtiles = ((long long)max_blocks_per_seq * block_size + kTile - 1) / kTile;
-    const long long target = 2LL * cu_count();
-    const long long rows = (long long)num_seqs * num_kv_heads;
-    long long tpw = std::max(1LL, (rows * wtiles + ts * target - 1) / (ts * target));
-    long long chunk = ts * tpw;
-    long long parts = (wtiles + chunk - 1) / chunk;
-    if (parts > kMaxSplit) {
-        const long long need = (wtiles + kMaxSplit - 1) / kMaxSplit;
-        chunk = ((need + ts - 1) / ts) * ts;
-        parts = (wtiles + chunk - 1) / chunk;
-    }
-    const long long grid = rows * parts;
-    if (grid > 0x7fffffffLL || parts > max_parts_for(block_size, max_blocks_per_seq)) return PA_ERR_INVALID_ARG;
-    const int max_parts = max_parts_for(block_size, max_blocks_per_seq);
+    const Plan pl = make_plan(num_seqs, num_kv_heads, block_size, max_blocks_per_seq);
+    const int slots = blocks_per_cu(fn) * cu_count();
     char* ws = static_cast<char*>(workspace);
     int32_t* counters = reinterpret_cast<int32_t*>(ws);
     float* part_ml = reinterpret_cast<float*>(ws + counters_bytes(num_seqs, num_kv_heads));
-    float* part_acc = part_ml + (size_t)num_seqs * max_parts * num_heads * 2;
-    int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, ck = (int)chunk, np = (int)parts;
+    float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
     float sl2 = scale * 1.4426950408889634f;
-    void* args[] = {&out, (void*)&q, (void*)&k_pool, (void*)&v_pool, (void*)&block_tables, (void*)&seq_lens,
-                    &counters, &part_ml, &part_acc, &Hkv, &W, &N, &ck, &np, &sl2};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(kThreads), args, 0,
-                        (hipStream_t)stream) != hipSuccess)
-        return PA_ERR_HIP;
+    int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;
+    // Rows are processed kMaxRows at a time (the workgroups keep the rows'
+    // lengths in LDS); each launch covers its own rows of every buffer.
+    for (int r0 = 0; r0 < num_seqs; r0 += pl.rows) {
+        int Bc = std::min(pl.rows, num_seqs - r0);
+        const long long units_max = (long long)Bc * Hkv * P;
+        long long grid = std::min<long long>(slots, units_max);
+        grid = std::max(grid, (units_max + kMaxPending - 1) / kMaxPending);  // bounded list per workgroup
+        if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+        uint16_t* o = out + (size_t)r0 * num_heads * head_dim;
+        const uint16_t* qq = q + (size_t)r0 * num_heads * head_dim;
+        const int32_t* tt = block_tables + (size_t)r0 * max_blocks_per_seq;
+        const int32_t* ll = seq_lens + r0;
+        int32_t* cc = counters + (size_t)r0 * Hkv;
+        float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
+        float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
+        void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, &cc, &pm, &pa,
+                        &Bc, &Hkv, &W, &N, &C, &P, &sl2};
+        if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
+            hipSuccess)
+            return PA_ERR_HIP;
+    }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -65,14 +65,17 @@ def test_supported_shapes(pa):
 
 def test_workspace_size_arithmetic(pa):
     # counters (B*Hkv int32, rounded to 256 B) + B * partitions * Hq * (D+2) fp32,
-    # partitions = min(16, ceil(ceil(W*bs/64) / 2))
+    # partitions = ceil(tiles / C), tiles = ceil(W*bs/64), C tiles per partition
+    # = max(ceil(tiles/64), ceil(min(B,512)*Hkv*tiles/1024)), at most tiles
     def expect(B, Hq, Hkv, D, bs, W):
         tiles = -(-W * bs // 64)
-        parts = min(16, -(-tiles // 2))
+        c = max(-(-tiles // 64), -(-(min(B, 512) * Hkv * tiles) // 1024))
+        c = max(1, min(c, tiles))
+        parts = -(-tiles // c)
         return -(-(B * Hkv * 4) // 256) * 256 + B * parts * Hq * (D + 2) * 4
 
     for args in [(32, 12, 2, 128, 64, 68), (95, 12, 2, 128, 16, 144), (4, 2, 1, 64, 16, 5), (1, 8, 8, 64, 128, 3),
-                 (2, 12, 2, 128, 64, 400)]:
+                 (2, 12, 2, 128, 64, 400), (1000, 12, 2, 128, 16, 300)]:
         assert pa.paged_decode_workspace_size(*args) == expect(*args)
     assert pa.paged_decode_workspace_size(4, 12, 5, 128, 64, 4) == 0
 
