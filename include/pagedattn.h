@@ -112,10 +112,8 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
  * Bytes of device workspace paged_decode_attn needs for these sizes: the
  * per-(row, KV head) arrival counters of the split-sequence reduction and the
  * fp32 partial results (max, sum, unnormalised output per query head) of up
- * to P sequence partitions per (row, KV head). With T = ceil(W*block_size/64)
- * tiles of 64 tokens in a full row, a partition is C tiles,
- * C = min(T, max(ceil(T/64), ceil(min(num_seqs,512)*num_kv_heads*T/1024), 1)),
- * and P = ceil(T/C) (at most 64).
+ * to P = min(64, T) sequence partitions per (row, KV head), T =
+ * ceil(W*block_size/64) being the number of 64-token tiles of a full row.
  * Returns 0 for invalid sizes.
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -295,37 +295,38 @@ __device__ __forceinline__ int clamp_block(int blk, int N) {
 
 constexpr int kMaxRows = 512;    // rows per launch (longer batches are split by the host)
 constexpr int kMaxParts = 64;    // partitions per (row, KV head)
-constexpr int kMaxPending = 128; // split partitions one workgroup may finish
+constexpr int kMaxPending = 4;   // split runs one workgroup may finish (at most its first and last)
 
-// Work decomposition. A row of length L has ceil(L/64) tiles of 64 tokens; a
-// partition ("unit") is up to C consecutive tiles of one (row, KV head); a
-// row has np = max(1, ceil(tiles/C)) partitions per KV head (one, with no
-// tiles, for L = 0). Every workgroup reads seq_lens at start and builds the
-// prefix count of units per row in LDS, so the unit list holds only real work
-// and is the same in every workgroup. Workgroup w then takes a consecutive
-// range of ceil(units/G) of them (G workgroups, a persistent grid sized to the
-// GPU).
-struct Unit {
-    int u;        // unit index; >= total means none
-    int k;        // ordinal of the unit within this workgroup
-    int b, g, p;  // row, KV head, partition
-    int np;       // partitions of this (row, KV head)
-    int L;        // row length
-    int t0, t1;   // tiles [t0, t1) of the row
-};
-
-// One step of the tile pipeline: a tile (or, for an empty row, none) of a unit.
+// Work decomposition. A row of length L has nt = ceil(L/64) tiles of 64
+// tokens per KV head (an empty row counts one tile, without data, so that its
+// zero output is written by someone). All tiles of the batch are numbered
+// row by row, KV head by KV head; workgroup w of the G' busy ones takes the
+// contiguous range [w*T/G', (w+1)*T/G') of the T tiles, so every workgroup has
+// the same work to within one tile whatever the length mix. Every workgroup
+// reads seq_lens at start and builds the prefix count of tiles per row in
+// LDS, so it finds its tiles without any host-side plan.
+//
+// A run is the part of one (row, KV head) inside one workgroup's range. A
+// (row, KV head) covered by a single workgroup is finished by it; otherwise
+// each covering workgroup stores one partial (max, sum, unnormalised output)
+// and the last to arrive merges them. G' is capped so that a workgroup gets
+// at least C tiles, which bounds the partials of a (row, KV head) by the
+// workspace's P.
 struct Pos {
-    Unit n;
-    int t;             // tile index within the row
+    int t;               // tile number in the batch; >= this workgroup's range end means none
+    int b, g;            // row, KV head
+    int tile;            // tile index within the row
+    int nt;              // tiles of the row (>= 1)
+    int L;               // row length (0: an empty row's only, data-less tile)
+    int k;               // ordinal of the run within this workgroup
+    int np, slot;        // workgroups covering the (row, KV head), and this one's index among them
+    int first, last;     // the run's first / last tile
     int e0, e1, e2, e3;  // physical blocks of the tile (e1..e3 used when blocks are shorter than a tile)
-    __device__ bool valid(int total) const { return n.u < total; }
-    __device__ bool has_tile() const { return t < n.t1; }
-    __device__ bool first() const { return t == n.t0; }
-    __device__ bool last() const { return t + 1 >= n.t1; }
+    __device__ bool valid(int t_end) const { return t < t_end; }
+    __device__ bool has_tile() const { return L > 0; }
 };
 
-// Row of unit u: the last row whose prefix count is <= u, by two rounds of a
+// Row of tile u: the last row whose prefix count is <= u, by two rounds of a
 // 64-lane search over the LDS prefix array pre[0..B].
 __device__ __forceinline__ int find_row(const int* pre, int B, int u, int lane) {
     const int S = (B + 63) / 64;  // rows per first-round lane
@@ -341,29 +342,32 @@ template <int BS, int D, int NREP>
 struct Cfg {
     static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
     static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
-    static constexpr int WPT = (NREP % 2 == 0) ? 2 : 1;   // waves per workgroup, sharing every tile
-    static constexpr int HPW = NREP / WPT;                 // query heads per wave
-    static constexpr int LPW = NJ / WPT;                   // load instructions per wave per K (or V) tile
+    static constexpr int WPT = (NREP % 2 == 0) ? 2 : 1;   // compute waves, sharing every tile
+    static constexpr int HPW = NREP / WPT;                 // query heads per compute wave
     static constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
     static constexpr int TILE = kTile * D;                 // halves per K (or V) tile
     static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
-    static constexpr int QI = (QC + 64 * WPT - 1) / (64 * WPT);  // q load instructions per wave
-    static constexpr int QBUF = QI * WPT * 64 * 8;         // halves per q buffer
-    static constexpr int THREADS = 64 * WPT;
+    static constexpr int QI = (QC + 63) / 64;              // q load instructions
+    static constexpr int QBUF = QI * 64 * 8;               // halves per q buffer
+    static constexpr int THREADS = 64 * (WPT + 1);         // the compute waves and one load wave
     static_assert(TPB <= 4, "block size of at least 16 tokens");
-    static_assert(NJ % WPT == 0, "load split");
 };
 
-// decode_kernel: persistent, one workgroup of WPT waves (two when the group's
-// query-head count is even, one otherwise) per slot. Both waves read every
-// tile, each for half of the group's query heads.
+// decode_kernel: persistent, one workgroup per slot: WPT compute waves (two
+// when the group's query-head count is even, one otherwise), which both read
+// every tile, each for its share of the group's query heads, and one load
+// wave that issues every tile load and waits for it. A wave that issues a
+// load stalls whenever the memory system is saturated; keeping all loads in
+// their own wave keeps those stalls off the compute waves.
 //
 // Tile pipeline (step j computes tile position P_j; buffers alternate by j):
-//   prologue:  issue K(P0), V(P0)
-//   step j:    wait K(P_j) -> barrier A -> [j = 0: issue K(P1)] issue V(P_{j+1}) into the V buffer
-//              freed by step j-1 -> QK + softmax on K(P_j) -> wait V(P_j) ->
-//              barrier B -> issue K(P_{j+2}) into the K buffer just read ->
-//              PV on V(P_j) -> if P_j ends its unit, store the unit's result
+//   prologue:  load wave issues K(P0), V(P0)
+//   step j:    load wave waits for K(P_j) -> barrier A -> load wave issues
+//              [j = 0: K(P1)] V(P_{j+1}) into the V buffer freed by step j-1
+//              and waits for V(P_j) while compute waves do QK + softmax on
+//              K(P_j) -> barrier B -> load wave issues K(P_{j+2}) into the K
+//              buffer just read while compute waves do PV on V(P_j) and, if
+//              P_j ends its unit, store the unit's result
 // so 1.5 tiles of loads are in flight during every compute phase, across unit
 // boundaries as well. The query of a unit is loaded into LDS with the K tile
 // of its first position.
@@ -379,8 +383,9 @@ struct Cfg {
 //
 // Results: a one-partition row writes fp16 output directly; otherwise the
 // partition writes (max, sum, unnormalised output) with coherent stores and is
-// listed; at exit the workgroup takes one arrival ticket per listed partition
-// and merges every (row, KV head) for which it was last, in partition order.
+// listed; at exit the workgroup adds the number of partitions it finished of
+// each (row, KV head) to that pair's arrival counter in one atomic, and merges
+// every pair whose count it completed, in partition order.
 template <int BS, int D, int NREP>
 __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
@@ -388,7 +393,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     int32_t* __restrict__ counters, float* __restrict__ part_ml, float* __restrict__ part_acc, int B, int Hkv,
     int W, int N, int C, int P, float scale_log2) {
     using K = Cfg<BS, D, NREP>;
-    constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, LPW = K::LPW, TPB = K::TPB;
+    constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
     constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
     static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 
@@ -405,13 +410,14 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wip = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in the workgroup
-    const int h0 = wip * HPW;                                   // its first query head within the group
+    const bool loader = wip == WPT;                             // the load wave
+    const int h0 = wip * HPW;                                   // a compute wave's first query head
     const int Hq = Hkv * NREP;
     const int G = gridDim.x;
     const int cap = W * BS;
     const int drow = lane & 7, vc = lane >> 3;  // V load lane: row within a row block, token chunk
 
-    // ---- unit list: lengths and the prefix count of units per row
+    // ---- tile list: lengths and the prefix count of tiles per row
     for (int r = tid; r < B; r += THREADS) {
         int L = seq_lens[r];
         L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -424,16 +430,12 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         int carry = 0;
         for (int r0 = 0; r0 < B; r0 += 64) {
             const int r = r0 + lane;
-            int nu = 0;
-            if (r < B) {
-                const int nt = (s_len[r] + kTile - 1) / kTile;
-                nu = Hkv * max(1, (nt + C - 1) / C);
-            }
-            int x = nu;
+            const int nt = r < B ? Hkv * max(1, (s_len[r] + kTile - 1) / kTile) : 0;
+            int x = nt;
 #pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const int y = __shfl_up(x, s);
-                if (lane >= s) x += y;
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const int y = __shfl_up(x, sh);
+                if (lane >= sh) x += y;
             }
             if (r < B) s_pre[r + 1] = carry + x;
             carry += __shfl(x, 63);
@@ -441,41 +443,25 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         if (lane == 0) s_pre[0] = 0;
     }
     __syncthreads();
-    const int total = __builtin_amdgcn_readfirstlane(s_pre[B]);
+    const int T = __builtin_amdgcn_readfirstlane(s_pre[B]);
+    const int Gb = min(G, max(1, T / C));  // busy workgroups: each gets at least C tiles
+    const int w = blockIdx.x;
+    const int t_begin = w < Gb ? (int)(((long long)w * T) / Gb) : 0;
+    const int t_end = w < Gb ? (int)(((long long)(w + 1) * T) / Gb) : 0;
+    auto owner = [&](int a) {  // the workgroup whose range holds tile a
+        return (int)((((long long)a + 1) * Gb + T - 1) / T) - 1;
+    };
     wait_vmem<0>();  // nothing of the prologue is left in flight: the count below starts at zero
     int vm_count = 0;
 
-    // workgroup w takes the consecutive units [w*per, (w+1)*per): the
-    // partitions of one (row, KV head) mostly land in one workgroup's range,
-    // so a workgroup rarely has more than one merge to do at exit
-    const int per = (total + G - 1) / G;
-    auto unit_at = [&](int k) {
-        Unit n;
-        n.k = k;
-        n.u = k < per ? (int)blockIdx.x * per + k : total;
-        n.b = n.g = n.p = n.L = n.t0 = n.t1 = 0;
-        n.np = 1;
-        if (n.u < total) {
-            n.b = find_row(s_pre, B, n.u, lane);
-            n.L = __builtin_amdgcn_readfirstlane(s_len[n.b]);
-            const int nt = (n.L + kTile - 1) / kTile;
-            n.np = max(1, (nt + C - 1) / C);
-            const int r = n.u - __builtin_amdgcn_readfirstlane(s_pre[n.b]);
-            n.g = r / n.np;
-            n.p = r - n.g * n.np;
-            n.t0 = n.p * C;
-            n.t1 = min(nt, n.t0 + C);
-        }
-        return n;
-    };
     // table entries of a position's tile (scalar loads; entries past the
     // row's last block are replaced by the tile's first, whose data is masked)
     auto load_entries = [&](Pos& s) {
         s.e0 = s.e1 = s.e2 = s.e3 = 0;
-        if (!s.valid(total) || !s.has_tile()) return;
-        const int32_t* trow = tables + (size_t)s.n.b * W;
-        const int n0 = (s.t * kTile) / BS;
-        const int nblk = (s.n.L + BS - 1) / BS;
+        if (!loader || !s.valid(t_end) || !s.has_tile()) return;
+        const int32_t* trow = tables + (size_t)s.b * W;
+        const int n0 = (s.tile * kTile) / BS;
+        const int nblk = (s.L + BS - 1) / BS;
         s.e0 = trow[n0];
         if constexpr (TPB > 1) {
             s.e1 = trow[n0 + 1 < nblk ? n0 + 1 : n0];
@@ -485,22 +471,37 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             }
         }
     };
-    auto first_pos = [&](int k) {
+    // the position of tile t (prev: the position before it in this range)
+    auto pos_at = [&](int t, const Pos& prev, bool has_prev) {
         Pos s;
-        s.n = unit_at(k);
-        s.t = s.n.t0;
+        if (t >= t_end) {
+            s = prev;
+            s.t = t_end;
+            return s;
+        }
+        if (has_prev && prev.tile + 1 < prev.nt) {  // the same run goes on
+            s = prev;
+            s.t = t;
+            s.tile = prev.tile + 1;
+            s.first = 0;
+        } else {
+            s.t = t;
+            s.b = find_row(s_pre, B, t, lane);
+            s.L = __builtin_amdgcn_readfirstlane(s_len[s.b]);
+            s.nt = max(1, (s.L + kTile - 1) / kTile);
+            const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
+            s.g = r / s.nt;
+            s.tile = r - s.g * s.nt;
+            const int a0 = t - s.tile;  // the (row, KV head)'s first tile
+            const int w0 = owner(a0);
+            s.np = owner(a0 + s.nt - 1) - w0 + 1;
+            s.slot = w - w0;
+            s.k = has_prev ? prev.k + 1 : 0;
+            s.first = 1;
+        }
+        s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
         load_entries(s);
         return s;
-    };
-    auto next_pos = [&](const Pos& s) {
-        if (!s.valid(total)) return s;
-        if (s.t + 1 < s.n.t1) {
-            Pos r = s;
-            r.t = s.t + 1;
-            load_entries(r);
-            return r;
-        }
-        return first_pos(s.n.k + 1);
     };
     auto entry_for = [&](const Pos& s, int idx) {  // idx = block of the tile (0..TPB-1), wave-divergent
         if constexpr (TPB == 1) {
@@ -512,38 +513,33 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         }
     };
 
-    // ---- loads into LDS (this wave's share of each)
+    // ---- loads into LDS (issued by the load wave only); LDS byte addresses
+    const unsigned lds_k = lds_addr(&s_k[0][0]), lds_v = lds_addr(&s_v[0][0]), lds_q = lds_addr(&s_q[0][0]);
     auto issue_q = [&](const Pos& s) {
-        const uint16_t* qrow = q + ((size_t)s.n.b * Hq + (size_t)s.n.g * NREP) * D;
+        const uint16_t* qrow = q + ((size_t)s.b * Hq + (size_t)s.g * NREP) * D;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
-            const int c = (i * WPT + wip) * 64 + lane;
-            dma16(qrow + 8 * min(c, QC - 1), lds_addr(&s_q[s.n.k & 1][(i * WPT + wip) * 512]));
+            const int c = i * 64 + lane;
+            dma16(qrow + 8 * min(c, QC - 1), lds_q + (unsigned)(((s.k & 1) * QBUF + i * 512) * 2));
         }
         vm_count += QI;
     };
     auto issue_k = [&](const Pos& s, int buf) {
-        const int tok = s.t * kTile + lane;
+        const int tok = s.tile * kTile + lane;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : lane / BS), N);
-        const uint16_t* src = k_pool + ((size_t)phys * Hkv + s.n.g) * (size_t)(D * BS) + (size_t)(tok % BS) * 8;
+        const uint16_t* src = k_pool + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)(tok % BS) * 8;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int j = i * WPT + wip;
-            dma16(src + (size_t)j * (BS * 8), lds_addr(&s_k[buf][j * 512]));
-        }
-        vm_count += LPW;
+        for (int j = 0; j < NJ; ++j) dma16(src + (size_t)j * (BS * 8), lds_k + (unsigned)((buf * TILE + j * 512) * 2));
+        vm_count += NJ;
     };
     auto issue_v = [&](const Pos& s, int buf) {
-        const int tok = s.t * kTile + 8 * vc;
+        const int tok = s.tile * kTile + 8 * vc;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (8 * vc) / BS), N);
         const uint16_t* src =
-            v_pool + ((size_t)phys * Hkv + s.n.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS);
+            v_pool + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int jj = i * WPT + wip;
-            dma16(src + (size_t)jj * (8 * BS), lds_addr(&s_v[buf][jj * 512]));
-        }
-        vm_count += LPW;
+        for (int jj = 0; jj < NJ; ++jj) dma16(src + (size_t)jj * (8 * BS), lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
+        vm_count += NJ;
     };
 
     // ---- per-unit state
@@ -551,11 +547,12 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     unsigned qr[HPW][QR];
     float m[HPW], lsum[HPW], acc[HPW][NH];
 
-    Pos P0 = first_pos(0);
-    Pos P1 = next_pos(P0);
-    Pos P2 = next_pos(P1);
+    const Pos none = {};
+    Pos P0 = pos_at(t_begin, none, false);
+    Pos P1 = pos_at(t_begin + 1, P0, true);
+    Pos P2 = pos_at(t_begin + 2, P1, true);
     int mk0 = 0, mk1 = 0, mv0 = 0, mv1 = 0;  // vm_count after each buffer's last load
-    if (P0.valid(total) && P0.has_tile()) {
+    if (loader && P0.valid(t_end) && P0.has_tile()) {
         issue_q(P0);
         issue_k(P0, 0);
         mk0 = vm_count;
@@ -563,24 +560,24 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         mv0 = vm_count;
     }
 
-    for (int j = 0; P0.valid(total); ++j) {
+    for (int j = 0; P0.valid(t_end); ++j) {
         const int buf = j & 1;
         const bool tile = P0.has_tile();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
+        if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
         tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
-        if (P1.valid(total) && P1.has_tile()) {
+        if (loader && P1.valid(t_end) && P1.has_tile()) {
             if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
-                if (P1.first()) issue_q(P1);
+                if (P1.first) issue_q(P1);
                 issue_k(P1, 1);
                 mk1 = vm_count;
             }
             issue_v(P1, buf ^ 1);
             if (buf) mv0 = vm_count; else mv1 = vm_count;
         }
-        if (tile) {
-            if (P0.first()) {
-                const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.n.k & 1][0]) + h0 * (D / 2);
+        if (!loader && tile) {
+            if (P0.first) {
+                const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.k & 1][0]) + h0 * (D / 2);
 #pragma unroll
                 for (int h = 0; h < HPW; ++h)
 #pragma unroll
@@ -594,7 +591,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
                 }
             }
             // ---- scores: lane = token, query pairs broadcast across lanes by DPP
-            const int t0 = P0.t * kTile;
+            const int t0 = P0.tile * kTile;
             u32x4 kj[NJ];
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj) kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][jj * 512 + lane * 8]);
@@ -611,7 +608,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
                     score_block<4 * (J % 4)>(a4, qj, kj[J]);
                 }(), ...);
             }(std::make_integer_sequence<int, NJ>{});
-            const bool live = t0 + lane < P0.n.L;
+            const bool live = t0 + lane < P0.L;
             float s[HPW];
 #pragma unroll
             for (int h = 0; h < HPW; ++h) {
@@ -639,16 +636,16 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
+        if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
         tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
-        if (P2.valid(total) && P2.has_tile()) {
-            if (P2.first()) issue_q(P2);
+        if (loader && P2.valid(t_end) && P2.has_tile()) {
+            if (P2.first) issue_q(P2);
             issue_k(P2, buf);
             if (buf) mk1 = vm_count; else mk0 = vm_count;
         }
-        if (tile) {
+        if (!loader && tile) {
             // ---- PV: lane = channel; chunk c of the tile read in the order c ^ par
-            const int t0 = P0.t * kTile;
+            const int t0 = P0.tile * kTile;
             const int par = vc & 1;  // parity of this lane's row block (lane / 8)
             const uint16_t* vb = &s_v[buf][(lane >> 3) * 512 + drow * 8];
             const _Float16* pb = &s_p[wip][0][0];
@@ -662,10 +659,10 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 #pragma unroll
                 for (int hv = 0; hv < NH; ++hv) vv[c][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8 * 512 + cc * 64);
             }
-            if (t0 + kTile > P0.n.L) {  // tokens past the row's end may hold NaN: zero their V
+            if (t0 + kTile > P0.L) {  // tokens past the row's end may hold NaN: zero their V
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const int n = P0.n.L - (t0 + 8 * (c ^ par));
+                    const int n = P0.L - (t0 + 8 * (c ^ par));
                     u32x4 mask;
                     mask.x = (n > 0 ? 0xffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
                     mask.y = (n > 2 ? 0xffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
@@ -682,13 +679,13 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 #pragma unroll
                     for (int h = 0; h < HPW; ++h) acc[h][hv] = dot8(pv[c][h], vv[c][hv], acc[h][hv]);
         }
-        if (P0.last()) {
+        if (!loader && P0.last) {
             // ---- the unit's result
-            const int b = P0.n.b, g = P0.n.g;
+            const int b = P0.b, g = P0.g;
             float lt[HPW];
 #pragma unroll
             for (int h = 0; h < HPW; ++h) lt[h] = tile ? wave_sum(lsum[h]) : 1.f;
-            if (P0.n.np == 1) {
+            if (P0.np == 1) {
                 uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + h0) * D + lane;
 #pragma unroll
                 for (int h = 0; h < HPW; ++h)
@@ -697,9 +694,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
                         const float o = tile ? acc[h][hv] / lt[h] : 0.f;
                         st_u16(orow + h * D + hv * 64, __builtin_bit_cast(uint16_t, (_Float16)o));
                     }
-                vm_count += HPW * NH;
             } else {
-                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.n.p) * NREP + h0;
+                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.slot) * NREP + h0;
                 float* pa = part_acc + slot * D + lane;
 #pragma unroll
                 for (int h = 0; h < HPW; ++h)
@@ -710,12 +706,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 #pragma unroll
                     for (int h = 0; h < HPW; ++h) st_2f32_sc1(pm + 2 * h, m[h], lt[h]);
                 }
-                vm_count += HPW * NH + HPW;
                 if (wip == 0 && lane == 0) {
                     const int n = s_npend;
                     if (n < kMaxPending) {
                         s_pend[n] = b * Hkv + g;
-                        s_pend_np[n] = P0.n.np;
+                        s_pend_np[n] = P0.np;
                         s_npend = n + 1;
                     }
                 }
@@ -723,7 +718,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         }
         P0 = P1;
         P1 = P2;
-        P2 = next_pos(P2);
+        P2 = pos_at(P2.t + 1, P2, true);
     }
 
     // ---- tickets and merges of split (row, KV head)s
@@ -732,7 +727,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     const int npend = __builtin_amdgcn_readfirstlane(s_npend);
     for (int e = tid; e < npend; e += THREADS) {
         const int t = __hip_atomic_fetch_add(&counters[s_pend[e]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_pend_np[e] = (t == s_pend_np[e] - 1) ? s_pend_np[e] : -s_pend_np[e];  // > 0: this workgroup merges
+        s_pend_np[e] = (t + 1 == s_pend_np[e]) ? s_pend_np[e] : -s_pend_np[e];  // > 0: this workgroup merges
     }
     __syncthreads();
     // Merge: every thread owns 4-channel chunks of the group's output and
@@ -740,7 +735,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     // their loads in flight together (running max, rescaled sums).
     constexpr int NC4 = NREP * D / 4;
     constexpr int CPT = (NC4 + THREADS - 1) / THREADS;  // chunks per thread
-    constexpr int MB = 8;                               // partitions per round trip
+    constexpr int MB = CPT == 1 ? 16 : 8;               // partitions per round trip
     for (int e = 0; e < npend; ++e) {
         const int np = __builtin_amdgcn_readfirstlane(s_pend_np[e]);
         if (np <= 0) continue;
@@ -920,25 +915,23 @@ DecodeFn pick_decode(int bs, int D, int nrep) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Partition plan, fixed on the host from sizes alone (no device value is
-// read): C tiles per partition, so that a batch whose rows all fill the
-// table width gives about 1024 partitions (several per workgroup slot of
-// the GPU, for balance), with at most kMaxParts partitions per row.
+// Split bounds, fixed on the host from sizes alone (no device value is read):
+// at most P = min(kMaxParts, tiles of a full row) partials per (row, KV head),
+// which holds when every busy workgroup takes at least C tiles.
 struct Plan {
     long long wtiles;  // tiles of a full-width row
     int rows;          // rows per launch
-    int C;             // tiles per partition
-    int P;             // partitions per (row, KV head), at most
+    int C;             // tiles per busy workgroup, at least
+    int P;             // partials per (row, KV head), at most
 };
 
 Plan make_plan(int B, int Hkv, int bs, int W) {
     Plan pl;
     pl.wtiles = ((long long)W * bs + kTile - 1) / kTile;
     pl.rows = std::max(1, std::min(B, kMaxRows));
-    const long long work = (long long)pl.rows * Hkv * pl.wtiles;
-    const long long c = std::max((pl.wtiles + kMaxParts - 1) / kMaxParts, (work + 1023) / 1024);
-    pl.C = (int)std::max(1LL, std::min(c, pl.wtiles));
-    pl.P = (int)((pl.wtiles + pl.C - 1) / pl.C);
+    pl.P = (int)std::min<long long>(kMaxParts, pl.wtiles);
+    // a (row, KV head) of nt tiles meets at most 1 + ceil((nt-1)/C) ranges of >= C tiles
+    pl.C = pl.P > 1 ? (int)((pl.wtiles - 1 + pl.P - 2) / (pl.P - 1)) : 1;
     return pl;
 }
 
@@ -1070,10 +1063,7 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
     // lengths in LDS); each launch covers its own rows of every buffer.
     for (int r0 = 0; r0 < num_seqs; r0 += pl.rows) {
         int Bc = std::min(pl.rows, num_seqs - r0);
-        const long long units_max = (long long)Bc * Hkv * P;
-        long long grid = std::min<long long>(slots, units_max);
-        grid = std::max(grid, (units_max + kMaxPending - 1) / kMaxPending);  // bounded list per workgroup
-        if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+        const long long grid = std::min<long long>(slots, (long long)Bc * Hkv * pl.wtiles);
         uint16_t* o = out + (size_t)r0 * num_heads * head_dim;
         const uint16_t* qq = q + (size_t)r0 * num_heads * head_dim;
         const int32_t* tt = block_tables + (size_t)r0 * max_blocks_per_seq;

@@ -65,13 +65,10 @@ def test_supported_shapes(pa):
 
 def test_workspace_size_arithmetic(pa):
     # counters (B*Hkv int32, rounded to 256 B) + B * partitions * Hq * (D+2) fp32,
-    # partitions = ceil(tiles / C), tiles = ceil(W*bs/64), C tiles per partition
-    # = max(ceil(tiles/64), ceil(min(B,512)*Hkv*tiles/1024)), at most tiles
+    # partitions = min(64, tiles), tiles = ceil(W*bs/64)
     def expect(B, Hq, Hkv, D, bs, W):
         tiles = -(-W * bs // 64)
-        c = max(-(-tiles // 64), -(-(min(B, 512) * Hkv * tiles) // 1024))
-        c = max(1, min(c, tiles))
-        parts = -(-tiles // c)
+        parts = min(64, tiles)
         return -(-(B * Hkv * 4) // 256) * 256 + B * parts * Hq * (D + 2) * 4
 
     for args in [(32, 12, 2, 128, 64, 68), (95, 12, 2, 128, 16, 144), (4, 2, 1, 64, 16, 5), (1, 8, 8, 64, 128, 3),
