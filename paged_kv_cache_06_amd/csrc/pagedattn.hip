@@ -342,8 +342,8 @@ template <int BS, int D, int NREP>
 struct Cfg {
     static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
     static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
-    static constexpr int WPT = (NREP % 2 == 0) ? 2 : 1;   // compute waves, sharing every tile
-    static constexpr int HPW = NREP / WPT;                 // query heads per compute wave
+    static constexpr int HPW = (NREP % 2 == 0) ? 2 : 1;   // query heads per compute wave
+    static constexpr int WPT = NREP / HPW;                 // compute waves, sharing every tile
     static constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
     static constexpr int TILE = kTile * D;                 // halves per K (or V) tile
     static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
@@ -353,10 +353,10 @@ struct Cfg {
     static_assert(TPB <= 4, "block size of at least 16 tokens");
 };
 
-// decode_kernel: persistent, one workgroup per slot: WPT compute waves (two
-// when the group's query-head count is even, one otherwise), which both read
-// every tile, each for its share of the group's query heads, and one load
-// wave that issues every tile load and waits for it. A wave that issues a
+// decode_kernel: persistent, one workgroup per slot: WPT compute waves (one
+// per two query heads of the group, or one for a single head), which all read
+// every tile, each for its own query heads, and one load wave that issues
+// every tile load and waits for it. A wave that issues a
 // load stalls whenever the memory system is saturated; keeping all loads in
 // their own wave keeps those stalls off the compute waves.
 //
