@@ -110,10 +110,12 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
 
 /*
  * Bytes of device workspace paged_decode_attn needs for these sizes: the
- * per-(row, KV head) arrival counters of the split-sequence reduction and the
  * fp32 partial results (max, sum, unnormalised output per query head) of up
  * to P = min(64, T) sequence partitions per (row, KV head), T =
- * ceil(W*block_size/64) being the number of 64-token tiles of a full row.
+ * ceil(W*block_size/64) being the number of 64-token tiles of a full row,
+ * rounded up to 256 bytes, then the per-(row, KV head) int32 arrival counters
+ * of the split-sequence reduction, rounded up to 256 bytes. The value never
+ * decreases when any argument grows.
  * Returns 0 for invalid sizes.
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -122,8 +124,11 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
 /*
  * Zero a workspace with a device fill kernel (no memset, so it may be
  * captured in a HIP graph). A workspace must be all-zero before its first
- * paged_decode_attn call; every completed call leaves its counters at zero
- * again, so one init per allocation suffices.
+ * paged_decode_attn call. The partials sit at its start and the counters at
+ * its end, and every completed call leaves its counters at zero again, so
+ * one init per allocation suffices for any sequence of calls whose sizes the
+ * workspace covers (e.g. sized with the largest num_seqs and
+ * max_blocks_per_seq used).
  */
 pa_status paged_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

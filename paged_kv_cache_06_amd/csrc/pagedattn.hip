@@ -935,7 +935,14 @@ Plan make_plan(int B, int Hkv, int bs, int W) {
     return pl;
 }
 
-size_t counters_bytes(int B, int Hkv) { return (((size_t)B * Hkv * 4) + 255) / 256 * 256; }
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t counters_bytes(int B, int Hkv) { return round256((size_t)B * Hkv * 4); }
+size_t partials_bytes(int B, int Hq, int D, int P) { return round256((size_t)B * P * Hq * (D + 2) * 4); }
+
+// Workspace layout: the partials from the start, the arrival counters at the
+// (256-byte aligned) end. Every call leaves its counters at zero, so a
+// workspace sized for a shape that bounds every call made with it serves all
+// of them: no call's partials reach into any call's counters.
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -1020,7 +1027,7 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
         return 0;
     const size_t rows = (size_t)(num_seqs > 0 ? num_seqs : 1);
     const Plan pl = make_plan((int)rows, num_kv_heads, block_size, max_blocks_per_seq);
-    return counters_bytes((int)rows, num_kv_heads) + rows * (size_t)pl.P * num_heads * (head_dim + 2) * 4;
+    return partials_bytes((int)rows, num_heads, head_dim, pl.P) + counters_bytes((int)rows, num_kv_heads);
 }
 
 pa_status paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -1054,8 +1061,8 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
     const Plan pl = make_plan(num_seqs, num_kv_heads, block_size, max_blocks_per_seq);
     const int slots = blocks_per_cu(fn) * cu_count();
     char* ws = static_cast<char*>(workspace);
-    int32_t* counters = reinterpret_cast<int32_t*>(ws);
-    float* part_ml = reinterpret_cast<float*>(ws + counters_bytes(num_seqs, num_kv_heads));
+    int32_t* counters = reinterpret_cast<int32_t*>(ws + (workspace_bytes / 256 * 256 - counters_bytes(num_seqs, num_kv_heads)));
+    float* part_ml = reinterpret_cast<float*>(ws);
     float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
     float sl2 = scale * 1.4426950408889634f;
     int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;

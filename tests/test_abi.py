@@ -64,12 +64,12 @@ def test_supported_shapes(pa):
 
 
 def test_workspace_size_arithmetic(pa):
-    # counters (B*Hkv int32, rounded to 256 B) + B * partitions * Hq * (D+2) fp32,
+    # B * partitions * Hq * (D+2) fp32 + counters (B*Hkv int32), each rounded to 256 B,
     # partitions = min(64, tiles), tiles = ceil(W*bs/64)
     def expect(B, Hq, Hkv, D, bs, W):
         tiles = -(-W * bs // 64)
         parts = min(64, tiles)
-        return -(-(B * Hkv * 4) // 256) * 256 + B * parts * Hq * (D + 2) * 4
+        return -(-(B * Hkv * 4) // 256) * 256 + -(-(B * parts * Hq * (D + 2) * 4) // 256) * 256
 
     for args in [(32, 12, 2, 128, 64, 68), (95, 12, 2, 128, 16, 144), (4, 2, 1, 64, 16, 5), (1, 8, 8, 64, 128, 3),
                  (2, 12, 2, 128, 64, 400), (1000, 12, 2, 128, 16, 300)]:

@@ -244,6 +244,63 @@ def test_one_very_long_row_uses_many_partitions(torch, pa, oracle):
     assert_close(out, ref, "long row")
 
 
+def _check_lengths(torch, pa, oracle, lens, bs=64, heads=(12, 2), D=128, seed=11, label=""):
+    Hq, Hkv = heads
+    N = sum(wl.blocks_for(L, bs) for L in lens) + 8
+    w = wl.make_workload(label or "lens", len(lens), Hq, Hkv, D, bs, N, lens, seed=seed, events=20)
+    ld = w.layer(0)
+    wl.poison_stale(ld.k_pool, ld.v_pool, w.tables, w.seq_lens, w.bs)
+    out = host(run_decode(torch, pa, w, upload(torch, w, ld)))
+    ref, _ = oracle.paged_decode_attn(ld.q, ld.k_pool, ld.v_pool, w.tables, w.seq_lens, w.bs, w.scale,
+                                      nthreads=NTHREADS)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b].view(np.uint16) == 0), f"row {b} has length 0 but a nonzero output"
+    return assert_close(out, ref, label)
+
+
+def test_more_rows_than_one_launch_takes(torch, pa, oracle):
+    # 1100 short rows (zero-length ones among them): the host runs the kernel
+    # over several row ranges, each with its own slice of every buffer.
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(0, 300, size=1100)]
+    lens[0] = lens[517] = lens[1099] = 0
+    say("1100 rows")
+    _check_lengths(torch, pa, oracle, lens, bs=16, label="1100 rows")
+
+
+def test_long_rows_share_workgroups_at_the_split_bound(torch, pa, oracle):
+    # A table 300 tiles wide: partials per (row, KV head) reach the bound of
+    # 64, and long and short rows share workgroup ranges.
+    lens = [19200, 1, 4097, 0, 63, 19135]
+    say("rows of 19200 tokens")
+    _check_lengths(torch, pa, oracle, lens, bs=64, label="split bound")
+
+
+def test_all_rows_empty(torch, pa, oracle):
+    say("all rows empty")
+    _check_lengths(torch, pa, oracle, [0, 0, 0, 0, 0], bs=16, heads=(8, 8), D=64, label="empty rows")
+
+
+def test_one_workspace_for_different_batches(torch, pa, oracle):
+    # Arrival counters come back to zero after every call, so one workspace
+    # serves batches of different shapes in any order.
+    wa = wl.CONFIGS["mixed"]()
+    wb = wl.make_workload("other", 7, 12, 2, 128, 64, 200, [5000, 3, 700, 0, 64, 1300, 4097], seed=12, events=10)
+    ws = pa.new_workspace(max(wa.B, wb.B), 12, 2, 128, 64, max(wa.W, wb.W))
+    res = {}
+    for name, w in [("a", wa), ("b", wb), ("a2", wa), ("b2", wb)]:
+        ld = w.layer(0)
+        res[name] = host(run_decode(torch, pa, w, upload(torch, w, ld), ws=ws))
+        say("shared workspace", name)
+    for a, b in [("a", "a2"), ("b", "b2")]:
+        assert np.array_equal(res[a].view(np.uint16), res[b].view(np.uint16))
+    ld = wb.layer(0)
+    ref, _ = oracle.paged_decode_attn(ld.q, ld.k_pool, ld.v_pool, wb.tables, wb.seq_lens, wb.bs, wb.scale,
+                                      nthreads=NTHREADS)
+    assert_close(res["b"], ref, "shared workspace")
+
+
 def test_unsupported_shape_raises(torch, pa):
     q = torch.zeros(2, 12, 128, dtype=torch.float16, device="cuda")
     k = torch.zeros(8, 2, 16, 8, 8, dtype=torch.float16, device="cuda")
