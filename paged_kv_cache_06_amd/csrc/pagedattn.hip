@@ -811,29 +811,53 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 // ---------------------------------------------------------------------------
 
 // One wave per (row, KV head): lanes 0..D/8-1 copy the 16-byte K groups,
-// every lane copies D/64 (or fewer) V channels.
+// every lane copies D/64 (or fewer) V channels. The new token's K and V are
+// requested before the row's length and table entry, which they do not depend
+// on, so the call costs two dependent memory round trips instead of three.
 __global__ void __launch_bounds__(64) append_kernel(const uint16_t* __restrict__ k_new,
                                                     const uint16_t* __restrict__ v_new,
                                                     uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
                                                     const int32_t* __restrict__ tables,
                                                     const int32_t* __restrict__ seq_lens, int Hkv, int D, int BS,
                                                     int W, int N) {
+    constexpr int kMaxV = 8;  // V channels per lane held in registers (D <= 512)
     const int bg = blockIdx.x;
     const int b = bg / Hkv, g = bg % Hkv;
-    const int L = seq_lens[b];
-    if (L < 1 || (long long)L > (long long)W * BS) return;
-    const int pos = L - 1;
-    const int blk = tables[(size_t)b * W + pos / BS];
-    if (blk < 0 || blk >= N) return;
-    const int slot = pos % BS;
-    const size_t base = (size_t)blk * Hkv + g;
+    const int lane = threadIdx.x;
     const uint16_t* ksrc = k_new + ((size_t)b * Hkv + g) * D;
     const uint16_t* vsrc = v_new + ((size_t)b * Hkv + g) * D;
-    for (int j = threadIdx.x; j < D / 8; j += 64) {
+    const bool fast = D <= 64 * kMaxV;
+    // Issued from assembly, at clamped (always valid) addresses, so that the
+    // compiler neither sinks them below the length and table reads nor waits
+    // for them early; the wait comes right before the stores.
+    u32x4 kx;
+    unsigned vx[kMaxV];
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kx) : "v"(ksrc + 8 * min(lane, D / 8 - 1)) : "memory");
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i)
+        asm volatile("global_load_ushort %0, %1, off" : "=v"(vx[i]) : "v"(vsrc + min(lane + 64 * i, D - 1)) : "memory");
+    const int L = seq_lens[b];
+    const bool live = L >= 1 && (long long)L <= (long long)W * BS;
+    const int pos = live ? L - 1 : 0;
+    const int blk = tables[(size_t)b * W + pos / BS];
+    asm volatile("s_waitcnt vmcnt(0)"  // the loads above have landed (also before leaving early)
+                 : "+v"(kx), "+v"(vx[0]), "+v"(vx[1]), "+v"(vx[2]), "+v"(vx[3]), "+v"(vx[4]), "+v"(vx[5]),
+                   "+v"(vx[6]), "+v"(vx[7])::"memory");
+    if (!live || blk < 0 || blk >= N) return;
+    const int slot = pos % BS;
+    const size_t base = (size_t)blk * Hkv + g;
+    if (fast) {
+        if (lane < D / 8) *reinterpret_cast<u32x4*>(k_pool + ((base * (D / 8) + lane) * BS + slot) * 8) = kx;
+#pragma unroll
+        for (int i = 0; i < kMaxV; ++i)
+            if (lane + 64 * i < D) v_pool[(base * D + lane + 64 * i) * BS + slot] = (uint16_t)vx[i];
+        return;
+    }
+    for (int j = lane; j < D / 8; j += 64) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(ksrc + 8 * j);
         *reinterpret_cast<u32x4*>(k_pool + ((base * (D / 8) + j) * BS + slot) * 8) = x;
     }
-    for (int d = threadIdx.x; d < D; d += 64) v_pool[(base * D + d) * BS + slot] = vsrc[d];
+    for (int d = lane; d < D; d += 64) v_pool[(base * D + d) * BS + slot] = vsrc[d];
 }
 
 // One workgroup per (row, KV head, logical block); thread per (token, channel).
