@@ -3,7 +3,9 @@
 A step is one pass of the whole hot path over one batch: kv_append (the
 step's new K/V scattered into each row's last block) then paged_decode_attn
 (every row's blocks gathered at its own length, grouped-query attention for
-one query token), for every layer of the workload.
+one query token), for every layer of the workload. The timed step issues both
+as one launch per layer (paged_decode_attn_append); the same step issued as
+the two separate calls is timed beside it (`two_call_ms_per_step`).
 
 Default workload: batch 32, Qwen2.5-1.5B attention shape (12 query heads,
 2 KV heads, head_dim 128, fp16), block 64, every row at length 1024, blocks
@@ -15,11 +17,12 @@ from HBM rather than the 256 MB last-level cache.
 Output: one JSON line. `value` is algorithmic bytes moved per step (every
 row's K and V at its own length, q, out, table entries, lengths, and the
 append's reads and writes) divided by the measured time per step. The
-`roofline` object reports the decode kernel alone: its algorithmic bytes per
-launch over its average duration, measured with HIP events on the launch
-stream around launches issued back to back (events bracketing each single
-launch add a few microseconds of their own; that figure is
-`decode_us_bracketed`), against 8 TB/s. `cpu_baseline` times the CPU oracle on a
+`roofline` object reports the decode kernel alone, as the step launches it
+(with the append fused in): its algorithmic bytes per launch over its average
+duration, measured with HIP events on the launch stream around launches
+issued back to back (events bracketing each single launch add a few
+microseconds of their own; that figure is `decode_us_bracketed`), against
+8 TB/s. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
 
 `roofline.traffic` is the decode kernel's HBM bytes per launch from two
@@ -133,7 +136,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, 
     w_scale = copy_bytes / (w_cpy * 1024.0)
     traffic = f_dec * 1024.0 * f_scale + w_dec * 1024.0 * w_scale
     w = wl.CONFIGS[workload]()
-    algo = decode_bytes(w, unique=True)
+    algo = decode_bytes(w, unique=True) + append_bytes(w)
     lines = [
         f"# decode_kernel HBM traffic, workload {workload}",
         f"# command: {command}",
@@ -236,23 +239,31 @@ def main():
 
     def step(i):
         for q, kn, vn, kp, vp in sets[i % R]:
+            pa.paged_decode_attn_append(q, kn, vn, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
+
+    def step_two_calls(i):
+        for q, kn, vn, kp, vp in sets[i % R]:
             pa.kv_append(kn, vn, kp, vp, tables, lens, w.bs)
             pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
 
-    # ---- whole-step throughput
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    def time_steps(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
 
-    # ---- per-launch durations of each kernel (events around each launch)
+    # ---- whole-step throughput (the two-call form of the same step beside it)
+    ms_per_step = time_steps(step)
+    two_call_ms_per_step = time_steps(step_two_calls)
+
+    # ---- per-launch durations (events around each launch)
     n_k = max(20, min(args.steps, 400))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
@@ -262,28 +273,36 @@ def main():
         pa.kv_append(kn, vn, kp, vp, tables, lens, w.bs)
         ev_a[i][1].record()
         ev[i][0].record()
-        pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
+        pa.paged_decode_attn_append(q, kn, vn, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
         ev[i][1].record()
     torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     app_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_a]))
-    # decode launches back to back on the same stream: the average gap between
-    # consecutive completions, i.e. the kernel's duration without launch gaps
-    b0 = torch.cuda.Event(enable_timing=True)
-    b1 = torch.cuda.Event(enable_timing=True)
-    b0.record()
-    for i in range(n_k):
-        q, kn, vn, kp, vp = sets[i % R][i % layers]
-        pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
-    b1.record()
-    torch.cuda.synchronize()
-    dec_b2b_ms = b0.elapsed_time(b1) / n_k
 
-    step_bytes = (decode_bytes(w) + append_bytes(w)) * layers
-    unique_step_bytes = (decode_bytes(w, unique=True) + append_bytes(w)) * layers
+    # launches back to back on the same stream: the average gap between
+    # consecutive completions, i.e. a kernel's duration without launch gaps
+    def back_to_back(call):
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for i in range(n_k):
+            call(*sets[i % R][i % layers])
+        b1.record()
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / n_k
+
+    dec_b2b_ms = back_to_back(lambda q, kn, vn, kp, vp: pa.paged_decode_attn_append(
+        q, kn, vn, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws))
+    dec_only_b2b_ms = back_to_back(lambda q, kn, vn, kp, vp: pa.paged_decode_attn(
+        q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws))
+
+    launch_bytes = decode_bytes(w) + append_bytes(w)
+    unique_launch_bytes = decode_bytes(w, unique=True) + append_bytes(w)
+    step_bytes = launch_bytes * layers
+    unique_step_bytes = unique_launch_bytes * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = decode_bytes(w) / (dec_b2b_ms * 1e-3) / 1e9
-    dec_unique_gbs = decode_bytes(w, unique=True) / (dec_b2b_ms * 1e-3) / 1e9
+    dec_gbs = launch_bytes / (dec_b2b_ms * 1e-3) / 1e9
+    dec_unique_gbs = unique_launch_bytes / (dec_b2b_ms * 1e-3) / 1e9
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -348,8 +367,11 @@ def main():
         "rows_layers_per_s": round(w.B * layers / (ms_per_step * 1e-3), 1),
         "bytes_per_step": step_bytes,
         "unique_bytes_per_step": unique_step_bytes,
+        "two_call_ms_per_step": round(two_call_ms_per_step, 6),
+        "two_call_value": round(step_bytes / (two_call_ms_per_step * 1e-3) / 1e9, 2),
         "decode_us": round(dec_b2b_ms * 1e3, 3),
         "decode_us_bracketed": round(dec_ms * 1e3, 3),
+        "decode_without_append_us": round(dec_only_b2b_ms * 1e3, 3),
         "append_us": round(app_ms * 1e3, 3),
         "roofline": {
             "bound": "hbm",
@@ -359,7 +381,7 @@ def main():
             "frac": round(dec_unique_gbs / PEAK_HBM_GBS, 4),
             "traffic": read_traffic(w.name),
             "kernel": "decode_kernel",
-            "bytes_per_launch": decode_bytes(w, unique=True),
+            "bytes_per_launch": unique_launch_bytes,
             "logical_GBs": round(dec_gbs, 2),
         },
         "cpu_baseline": cpu,

@@ -161,6 +161,32 @@ pa_status paged_decode_attn(uint16_t *out, const uint16_t *q, const uint16_t *k_
                             size_t workspace_bytes, void *stream);
 
 /*
+ * paged_decode_attn_append -- kv_append followed by paged_decode_attn, in one
+ * launch: a decode step's two calls [SLM paged attention, "End-to-end flow":
+ * the new token's K/V enter the row's last block, then attention runs over the
+ * row's blocks at its new length]. The results are bit-identical to
+ *     kv_append(k_new, v_new, k_pool, v_pool, ...);
+ *     paged_decode_attn(out, q, k_pool, v_pool, ...);
+ * on the same stream: the pools end up with the same bytes and `out` holds
+ * the same values. Inside the launch the workgroup that owns a row's last tile
+ * takes the new token's K/V straight from k_new / v_new (staged in LDS), so no
+ * read depends on the write, and stores them into the pool for later steps.
+ * Same arguments, alignment, workspace and errors as paged_decode_attn, plus
+ * k_new, v_new: [num_seqs][num_kv_heads][head_dim] fp16, 16-byte aligned,
+ * non-null. The append side follows kv_append: nothing is written for rows
+ * with L < 1, L > W*block_size or a target block id outside [0, N) (for the
+ * last, the attention result is unspecified, as is paged_decode_attn's for an
+ * invalid table entry). Appending into a block that another row reads in the
+ * same call (a shared block) is outside the contract, as for kv_append.
+ */
+pa_status paged_decode_attn_append(uint16_t *out, const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                   uint16_t *k_pool, uint16_t *v_pool, const int32_t *block_tables,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -10,6 +10,9 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   kv_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size,
                     scale, out=None, workspace=None)
+  paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables,
+                           seq_lens, block_size, scale, out=None,
+                           workspace=None)   (the two calls above, fused)
   paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                               block_size, max_blocks_per_seq)
@@ -60,6 +63,8 @@ def lib():
     L.paged_decode_workspace_init.restype = ctypes.c_int
     L.paged_decode_attn.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
     L.paged_decode_attn.restype = ctypes.c_int
+    L.paged_decode_attn_append.argtypes = [vp] * 8 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
+    L.paged_decode_attn_append.restype = ctypes.c_int
     L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
     L.paged_gather_kv.restype = ctypes.c_int
     _lib = L
@@ -162,6 +167,34 @@ def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, sca
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
     )
     _check(st, "paged_decode_attn")
+    return out
+
+
+def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size, scale, out=None,
+                             workspace=None, stream=None):
+    """kv_append(k_new, v_new, ...) then paged_decode_attn(q, ...), in one launch."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+    st = lib().paged_decode_attn_append(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_new, "k_new", torch.float16, 3), _dev(v_new, "v_new", torch.float16, 3),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
+    )
+    _check(st, "paged_decode_attn_append")
     return out
 
 

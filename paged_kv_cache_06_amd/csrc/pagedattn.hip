@@ -245,6 +245,12 @@ __device__ __forceinline__ void tile_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Wait for this wave's LDS operations only (lgkmcnt 0; vector-memory and
+// export counts left alone), before a barrier that publishes LDS writes.
+__device__ __forceinline__ void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<size_t>((lds_ptr)p));
 }
@@ -284,6 +290,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
     asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
 }
+__device__ __forceinline__ void st_b128(uint16_t* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
 
 __device__ __forceinline__ int clamp_block(int blk, int N) {
     return (unsigned)blk < (unsigned)N ? blk : 0;
@@ -296,6 +305,8 @@ __device__ __forceinline__ int clamp_block(int blk, int N) {
 constexpr int kMaxRows = 512;    // rows per launch (longer batches are split by the host)
 constexpr int kMaxParts = 64;    // partitions per (row, KV head)
 constexpr int kMaxPending = 4;   // split runs one workgroup may finish (at most its first and last)
+constexpr int kLenMask = 0x3fffffff;     // row length held in LDS ...
+constexpr int kLenNoSlot = 0x40000000;   // ... and a flag: the length exceeds the table, no slot to append into
 
 // Work decomposition. A row of length L has nt = ceil(L/64) tiles of 64
 // tokens per KV head (an empty row counts one tile, without data, so that its
@@ -322,6 +333,9 @@ struct Pos {
     int np, slot;        // workgroups covering the (row, KV head), and this one's index among them
     int first, last;     // the run's first / last tile
     int e0, e1, e2, e3;  // physical blocks of the tile (e1..e3 used when blocks are shorter than a tile)
+    int ap;              // the row takes this step's new token (fused append; L >= 1, within the table)
+    int nw;              // this tile holds that token (the row's last tile of an appending row)
+    int enew;            // physical block of that token (read by the wave that stores it)
     __device__ bool valid(int t_end) const { return t < t_end; }
     __device__ bool has_tile() const { return L > 0; }
 };
@@ -388,10 +402,10 @@ struct Cfg {
 // every pair whose count it completed, in partition order.
 template <int BS, int D, int NREP>
 __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
-    int32_t* __restrict__ counters, float* __restrict__ part_ml, float* __restrict__ part_acc, int B, int Hkv,
-    int W, int N, int C, int P, float scale_log2) {
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int32_t* __restrict__ counters, float* __restrict__ part_ml,
+    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2) {
     using K = Cfg<BS, D, NREP>;
     constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
     constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
@@ -401,6 +415,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t s_v[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QBUF];
     __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t s_kn[2][D];  // fused append: the new token's K ...
+    __shared__ __attribute__((aligned(16))) uint16_t s_vn[2][D];  // ... and V, staged with the tile holding it
     __shared__ int s_len[kMaxRows];
     __shared__ int s_pre[kMaxRows + 1];
     __shared__ int s_pend[kMaxPending];  // (row*Hkv + g) of split partitions finished here
@@ -416,12 +432,14 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     const int G = gridDim.x;
     const int cap = W * BS;
     const int drow = lane & 7, vc = lane >> 3;  // V load lane: row within a row block, token chunk
+    const bool append = k_new != nullptr;       // fused kv_append: this step's K/V enter the pool here
 
     // ---- tile list: lengths and the prefix count of tiles per row
     for (int r = tid; r < B; r += THREADS) {
         int L = seq_lens[r];
+        const int noslot = L > cap ? kLenNoSlot : 0;
         L = L < 0 ? 0 : (L > cap ? cap : L);
-        s_len[r] = L;
+        s_len[r] = L | noslot;
     }
     if (tid == 0) s_npend = 0;
     __syncthreads();
@@ -430,7 +448,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         int carry = 0;
         for (int r0 = 0; r0 < B; r0 += 64) {
             const int r = r0 + lane;
-            const int nt = r < B ? Hkv * max(1, (s_len[r] + kTile - 1) / kTile) : 0;
+            const int nt = r < B ? Hkv * max(1, ((s_len[r] & kLenMask) + kTile - 1) / kTile) : 0;
             int x = nt;
 #pragma unroll
             for (int sh = 1; sh < 64; sh <<= 1) {
@@ -487,7 +505,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         } else {
             s.t = t;
             s.b = find_row(s_pre, B, t, lane);
-            s.L = __builtin_amdgcn_readfirstlane(s_len[s.b]);
+            const int lf = __builtin_amdgcn_readfirstlane(s_len[s.b]);
+            s.L = lf & kLenMask;
+            s.ap = append && s.L > 0 && !(lf & kLenNoSlot);
             s.nt = max(1, (s.L + kTile - 1) / kTile);
             const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
             s.g = r / s.nt;
@@ -500,6 +520,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             s.first = 1;
         }
         s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
+        s.nw = s.ap && s.tile + 1 == s.nt;
+        s.enew = 0;
+        if (wip == 0 && s.nw) s.enew = tables[(size_t)s.b * W + (s.L - 1) / BS];
         load_entries(s);
         return s;
     };
@@ -515,6 +538,12 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 
     // ---- loads into LDS (issued by the load wave only); LDS byte addresses
     const unsigned lds_k = lds_addr(&s_k[0][0]), lds_v = lds_addr(&s_v[0][0]), lds_q = lds_addr(&s_q[0][0]);
+    const unsigned lds_kn = lds_addr(&s_kn[0][0]), lds_vn = lds_addr(&s_vn[0][0]);
+    // the new token's K (or V) of a tile that holds it, staged in LDS ahead of the tile's own loads
+    auto issue_new = [&](const Pos& s, const uint16_t* src, unsigned dst) {
+        if (lane < D / 8) dma16(src + ((size_t)s.b * Hkv + s.g) * D + 8 * lane, dst);
+        vm_count += 1;
+    };
     auto issue_q = [&](const Pos& s) {
         const uint16_t* qrow = q + ((size_t)s.b * Hq + (size_t)s.g * NREP) * D;
 #pragma unroll
@@ -525,6 +554,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         vm_count += QI;
     };
     auto issue_k = [&](const Pos& s, int buf) {
+        if (s.nw) issue_new(s, k_new, lds_kn + (unsigned)(buf * D * 2));
         const int tok = s.tile * kTile + lane;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : lane / BS), N);
         const uint16_t* src = k_pool + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)(tok % BS) * 8;
@@ -533,6 +563,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         vm_count += NJ;
     };
     auto issue_v = [&](const Pos& s, int buf) {
+        if (s.nw) issue_new(s, v_new, lds_vn + (unsigned)(buf * D * 2));
         const int tok = s.tile * kTile + 8 * vc;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (8 * vc) / BS), N);
         const uint16_t* src =
@@ -547,10 +578,10 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     unsigned qr[HPW][QR];
     float m[HPW], lsum[HPW], acc[HPW][NH];
 
+    // The first tile is requested as soon as its table entries are in; the
+    // entries of the next positions are requested after it.
     const Pos none = {};
     Pos P0 = pos_at(t_begin, none, false);
-    Pos P1 = pos_at(t_begin + 1, P0, true);
-    Pos P2 = pos_at(t_begin + 2, P1, true);
     int mk0 = 0, mk1 = 0, mv0 = 0, mv1 = 0;  // vm_count after each buffer's last load
     if (loader && P0.valid(t_end) && P0.has_tile()) {
         issue_q(P0);
@@ -559,13 +590,29 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         issue_v(P0, 0);
         mv0 = vm_count;
     }
+    Pos P1 = pos_at(t_begin + 1, P0, true);
+    Pos P2 = pos_at(t_begin + 2, P1, true);
 
     for (int j = 0; P0.valid(t_end); ++j) {
         const int buf = j & 1;
         const bool tile = P0.has_tile();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
+        if (loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int tn = P0.L - 1 - P0.tile * kTile;
+            if (lane < D / 8)
+                *reinterpret_cast<u32x4*>(&s_k[buf][lane * 512 + tn * 8]) =
+                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
+            wait_lds();
+        }
         tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
+        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N && lane < D / 8) {
+            // fused append: the new token's K into the pool (nothing in this launch reads it back)
+            const size_t base = (size_t)P0.enew * Hkv + P0.g;
+            st_b128(k_pool + ((base * (D / 8) + lane) * BS + (P0.L - 1) % BS) * 8,
+                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]));
+        }
         if (loader && P1.valid(t_end) && P1.has_tile()) {
             if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
                 if (P1.first) issue_q(P1);
@@ -575,6 +622,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             issue_v(P1, buf ^ 1);
             if (buf) mv0 = vm_count; else mv1 = vm_count;
         }
+        // the position after P2: its table entries are requested a whole step
+        // before anything waits on them
+        const Pos P3 = pos_at(P2.t + 1, P2, true);
         if (!loader && tile) {
             if (P0.first) {
                 const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.k & 1][0]) + h0 * (D / 2);
@@ -637,7 +687,26 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
+        if (loader && tile && P0.nw) {  // fused append: the new token's V into its slot of the tile
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int tn = P0.L - 1 - P0.tile * kTile;
+#pragma unroll
+            for (int hv = 0; hv < NH; ++hv) {
+                const int c = hv * 64 + lane;
+                s_v[buf][(c >> 3) * 512 + (tn >> 3) * 64 + (c & 7) * 8 + (tn & 7)] = s_vn[buf][c];
+            }
+            wait_lds();
+        }
         tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
+        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N) {
+            // fused append: the new token's V into the pool
+            const size_t base = (size_t)P0.enew * Hkv + P0.g;
+#pragma unroll
+            for (int hv = 0; hv < NH; ++hv) {
+                const int c = hv * 64 + lane;
+                st_u16(v_pool + (base * D + c) * BS + (P0.L - 1) % BS, s_vn[buf][c]);
+            }
+        }
         if (loader && P2.valid(t_end) && P2.has_tile()) {
             if (P2.first) issue_q(P2);
             issue_k(P2, buf);
@@ -718,7 +787,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         }
         P0 = P1;
         P1 = P2;
-        P2 = pos_at(P2.t + 1, P2, true);
+        P2 = P3;
     }
 
     // ---- tickets and merges of split (row, KV head)s
@@ -1063,11 +1132,17 @@ pa_status paged_decode_workspace_init(void* workspace, size_t workspace_bytes, v
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
-                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_decode_attn, and with k_new/v_new (non-null) the same launch with
+// kv_append of the step's K/V fused in.
+pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint16_t* v_pool,
+                        const int32_t* block_tables, const int32_t* seq_lens, const uint16_t* k_new,
+                        const uint16_t* v_new, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
@@ -1077,6 +1152,8 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_INVALID_ARG;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
     if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL / 2) return PA_ERR_INVALID_ARG;
     const size_t need = paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                                     max_blocks_per_seq);
@@ -1099,16 +1176,45 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
         const uint16_t* qq = q + (size_t)r0 * num_heads * head_dim;
         const int32_t* tt = block_tables + (size_t)r0 * max_blocks_per_seq;
         const int32_t* ll = seq_lens + r0;
+        const uint16_t* kn = k_new ? k_new + (size_t)r0 * num_kv_heads * head_dim : nullptr;
+        const uint16_t* vn = v_new ? v_new + (size_t)r0 * num_kv_heads * head_dim : nullptr;
         int32_t* cc = counters + (size_t)r0 * Hkv;
         float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
         float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
-        void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, &cc, &pm, &pa,
-                        &Bc, &Hkv, &W, &N, &C, &P, &sl2};
+        void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
+                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
             hipSuccess)
             return PA_ERR_HIP;
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    // the pools are only read on this path (no k_new: nothing is stored into them)
+    return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
+                         seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream);
+}
+
+pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                   uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+    return launch_decode(out, q, k_pool, v_pool, block_tables, seq_lens, k_new, v_new, num_seqs, num_heads,
+                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, workspace,
+                         workspace_bytes, stream);
 }
 
 pa_status paged_gather_kv(uint16_t* k_out, uint16_t* v_out, const uint16_t* k_pool, const uint16_t* v_pool,

@@ -31,8 +31,8 @@ def pa():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["kv_append", "paged_decode_attn", "paged_decode_workspace_size", "paged_decode_workspace_init",
-              "paged_gather_kv", "pa_status_string", "paged_decode_supported"]:
+    for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_workspace_size",
+              "paged_decode_workspace_init", "paged_gather_kv", "pa_status_string", "paged_decode_supported"]:
         assert n in names
 
 
@@ -102,6 +102,27 @@ def test_decode_rejects_bad_arguments_on_host(pa):
     assert _decode(L, ws=None) == 4
     assert _decode(L, ws=ctypes.c_void_p((1 << 20) + 64)) == 4  # workspace must be 256-byte aligned
     assert _decode(L, B=0) == 0  # nothing to do
+
+
+def _decode_append(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, t=FAKE, s=FAKE, B=4, Hq=12, Hkv=2, D=128, bs=64,
+             W=4, N=16, scale=0.1, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.paged_decode_attn_append(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["t"], a["s"], a["B"],
+                                      a["Hq"], a["Hkv"], a["D"], a["bs"], a["W"], a["N"],
+                                      ctypes.c_float(a["scale"]), a["ws"], a["wsb"], None)
+
+
+def test_fused_append_rejects_bad_arguments_on_host(pa):
+    L = pa.lib()
+    assert _decode_append(L, kn=None) == 1
+    assert _decode_append(L, vn=None) == 1
+    assert _decode_append(L, kn=ctypes.c_void_p((1 << 20) + 8)) == 1  # misaligned k_new
+    assert _decode_append(L, Hq=12, Hkv=5) == 1
+    assert _decode_append(L, q=None) == 1
+    assert _decode_append(L, bs=24) == 2
+    assert _decode_append(L, wsb=100) == 4
+    assert _decode_append(L, B=0) == 0  # nothing to do
 
 
 def test_append_and_gather_reject_bad_arguments_on_host(pa):
