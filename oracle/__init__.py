@@ -53,6 +53,8 @@ def _load(path=None):
     lib.oracle_float_to_half.restype = None
     lib.oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
     lib.oracle_kv_append.restype = ctypes.c_int
+    lib.oracle_kv_copy_blocks.argtypes = [u16p, u16p, i32p, i32p] + [i32] * 5
+    lib.oracle_kv_copy_blocks.restype = ctypes.c_int
     lib.oracle_gather_kv.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
     lib.oracle_gather_kv.restype = ctypes.c_int
     lib.oracle_paged_decode_attn.argtypes = [f32p, u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 7 + [
@@ -113,6 +115,21 @@ class Oracle:
             self._p(t, ctypes.c_int32),
             self._p(s, ctypes.c_int32),
             B, Hkv, D, bs, W, N,
+        )
+
+    def kv_copy_blocks(self, k_pool, v_pool, src, dst):
+        """In-place: block dst[i] <- block src[i] (K and V), pairs in order; returns the C status."""
+        N, Hkv = k_pool.shape[0], k_pool.shape[1]
+        D = v_pool.shape[2]
+        bs = v_pool.shape[3]
+        kp, vp = k_pool.view(np.uint16), v_pool.view(np.uint16)
+        s = np.ascontiguousarray(src, dtype=np.int32)
+        d = np.ascontiguousarray(dst, dtype=np.int32)
+        assert s.shape == d.shape and s.ndim == 1
+        return self.lib.oracle_kv_copy_blocks(
+            self._p(kp, ctypes.c_uint16), self._p(vp, ctypes.c_uint16),
+            self._p(s, ctypes.c_int32), self._p(d, ctypes.c_int32),
+            s.size, Hkv, D, bs, N,
         )
 
     def gather_kv(self, k_pool, v_pool, tables, seq_lens, bs, Hkv, D, fill=0):

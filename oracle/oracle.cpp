@@ -197,6 +197,34 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_p
     return rc;
 }
 
+// Copy whole blocks for copy-on-write: for each pair i in order, block dst[i]
+// takes block src[i]'s keys and values, every KV head and every slot. A block
+// shared by several rows is cloned before one of them writes into it, and
+// only that writer's table entry is repointed [SLM paged attention, "The
+// architecture: every piece explained" and "End-to-end flow"; PagedAttention,
+// "Sharing is the part that pays twice"]. A bit copy; no other block changes.
+// Returns 0, -1 on bad dimensions, or -2 if a pair names a block outside
+// [0, N) (that pair is skipped).
+int oracle_kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src, const int32_t *dst, int n,
+                          int Hkv, int D, int bs, int N) {
+    if (n < 0 || Hkv <= 0 || D <= 0 || D % 8 || bs <= 0 || N <= 0) return -1;
+    int rc = 0;
+    for (int i = 0; i < n; ++i) {
+        const int32_t s = src[i], t = dst[i];
+        if (s < 0 || s >= N || t < 0 || t >= N) {
+            rc = -2;
+            continue;
+        }
+        for (int g = 0; g < Hkv; ++g)
+            for (int slot = 0; slot < bs; ++slot)
+                for (int d = 0; d < D; ++d) {
+                    k_pool[k_index(t, g, slot, d, Hkv, D, bs)] = k_pool[k_index(s, g, slot, d, Hkv, D, bs)];
+                    v_pool[v_index(t, g, slot, d, Hkv, D, bs)] = v_pool[v_index(s, g, slot, d, Hkv, D, bs)];
+                }
+    }
+    return rc;
+}
+
 // Copy each row's first seq_len tokens out of the pool into contiguous
 // [B][Hkv][W*bs][D] arrays, walking the table; positions >= seq_len are left
 // untouched. This is the "read the same blocks" debug path [Paged attention,

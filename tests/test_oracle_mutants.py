@@ -38,6 +38,14 @@ MUTANTS = {
     "subnormal_scale": ("5.9604644775390625e-08f", "1.1920928955078125e-07f"),
     "exponent_bias": ("((expo - 15 + 127) << 23)", "((expo - 14 + 127) << 23)"),
     "round_half_up": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;", "if (rem >= 0x1000u) h += 1;"),
+    "copy_direction_swapped": (
+        "k_pool[k_index(t, g, slot, d, Hkv, D, bs)] = k_pool[k_index(s, g, slot, d, Hkv, D, bs)];",
+        "k_pool[k_index(s, g, slot, d, Hkv, D, bs)] = k_pool[k_index(t, g, slot, d, Hkv, D, bs)];",
+    ),
+    "copy_skips_last_slot": ("for (int slot = 0; slot < bs; ++slot)\n                for (int d = 0; d < D; ++d) {",
+                             "for (int slot = 0; slot < bs - 1; ++slot)\n                for (int d = 0; d < D; ++d) {"),
+    "copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)",
+                             "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)"),
 }
 
 FAST_PINS = [
@@ -54,6 +62,7 @@ FAST_PINS = [
     (pins.test_block_relabelling_invariance, {}),
     (pins.test_kv_append_matches_numpy_scatter, {"cfg": "tiny"}),
     (pins.test_kv_append_then_attention_sees_new_token, {}),
+    (pins.test_kv_copy_blocks_matches_numpy, {"shape": (2, 128, 64)}),
 ]
 
 

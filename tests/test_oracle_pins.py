@@ -378,6 +378,34 @@ def test_kv_append_then_attention_sees_new_token(oracle):
         assert np.array_equal(v[L - 1].view(np.uint16), ld.v_new[b].view(np.uint16))
 
 
+@pytest.mark.parametrize("shape", [(2, 128, 64), (1, 64, 16)])
+def test_kv_copy_blocks_matches_numpy(oracle, shape):
+    # Copy-on-write clones whole blocks: block dst[i] becomes block src[i]
+    # (K and V, every head and slot) and no other byte moves. Pinned against
+    # numpy's fancy-index assignment on disjoint pairs.
+    Hkv, D, bs = shape
+    N = 40
+    rng = np.random.default_rng(81)
+    kp = wl.normal_f16(rng, wl.k_pool_shape(N, Hkv, D, bs))
+    vp = wl.normal_f16(rng, wl.v_pool_shape(N, Hkv, D, bs))
+    perm = rng.permutation(N)
+    src, dst = perm[:9].astype(np.int32), perm[9:18].astype(np.int32)
+    k2, v2 = kp.copy(), vp.copy()
+    assert oracle.kv_copy_blocks(k2, v2, src, dst) == 0
+    ek, ev = kp.copy(), vp.copy()
+    ek[dst] = kp[src]
+    ev[dst] = vp[src]
+    assert np.array_equal(k2.view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(v2.view(np.uint16), ev.view(np.uint16))
+    # a pair naming a block outside the pool is skipped and reported
+    k3, v3 = kp.copy(), vp.copy()
+    assert oracle.kv_copy_blocks(k3, v3, np.array([N, 1], np.int32), np.array([2, 3], np.int32)) == -2
+    ek, ev = kp.copy(), vp.copy()
+    ek[3], ev[3] = kp[1], vp[1]
+    assert np.array_equal(k3.view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(v3.view(np.uint16), ev.view(np.uint16))
+
+
 def test_gather_matches_numpy(oracle):
     w = wl.make_workload("g", 5, 12, 2, 128, 16, 128, [0, 1, 16, 17, 300], seed=71, events=40)
     ld = w.layer(0)
