@@ -168,6 +168,68 @@ def append_bytes(w: wl.Workload) -> int:
     return rows * w.Hkv * w.D * 2 * 2 * 2 + rows * 4 + 4 * w.B
 
 
+def bench_copy_blocks(args, torch, pa):
+    """kv_copy_blocks alone: `--copy-pairs` random disjoint (src, dst) pairs of
+    a Qwen-shaped pool (2 KV heads, head_dim 128, block 64: 32 KiB of K and
+    32 KiB of V per block), one layer per call, replicas rotated so the copies
+    stream from HBM. Bytes per call: every copied block read once and written
+    once."""
+    Hkv, D, bs, N = 2, 128, 64, 4096
+    n = min(args.copy_pairs, N // 2)
+    block_bytes = Hkv * D * bs * 2 * 2  # K and V
+    pool_bytes = N * block_bytes
+    R = args.replicas or max(1, math.ceil((1 << 30) / pool_bytes))
+    rng = np.random.default_rng(17)
+    kp0 = torch.from_numpy(wl.normal_f16(rng, wl.k_pool_shape(N, Hkv, D, bs))).cuda()
+    vp0 = torch.from_numpy(wl.normal_f16(rng, wl.v_pool_shape(N, Hkv, D, bs))).cuda()
+    pools = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(R - 1)]
+    pairs = []
+    for r in range(R):
+        perm = rng.permutation(N).astype(np.int32)
+        pairs.append((torch.from_numpy(perm[:n].copy()).cuda(), torch.from_numpy(perm[n:2 * n].copy()).cuda()))
+    torch.cuda.synchronize()
+
+    def call(i):
+        kp, vp = pools[i % R]
+        src, dst = pairs[i % R]
+        pa.kv_copy_blocks(kp, vp, src, dst, bs)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        call(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    moved = 2 * n * block_bytes
+    gbs = moved / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "kv_copy_blocks (copy-on-write) achieved HBM GB/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "copy_blocks", "pairs": n, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "pool_blocks": N, "replicas": R, "bytes_per_call": moved},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
+                     "bytes_per_launch": moved},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +245,9 @@ def parse():
                     help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
     ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks"],
+                    help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone")
+    ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
     return ap.parse_args()
 
 
@@ -211,6 +276,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, torch, pa)
+        return
     w = wl.CONFIGS[args.config]()
     layers = w.layers
 

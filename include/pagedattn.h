@@ -187,6 +187,31 @@ pa_status paged_decode_attn_append(uint16_t *out, const uint16_t *q, const uint1
                                    size_t workspace_bytes, void *stream);
 
 /*
+ * kv_copy_blocks -- whole-block copies for copy-on-write: for every i <
+ * num_pairs, block dst[i] of both pools takes the contents of block src[i]
+ * (every KV head and every slot, K and V; a bit copy) [SLM paged attention,
+ * "The architecture: every piece explained": the manager clones the one
+ * shared block a sequence must write into and repoints that sequence's table
+ * entry, leaving the readers untouched; "End-to-end flow"; PagedAttention,
+ * "Sharing is the part that pays twice": a reference count and copy-on-write
+ * for the block that diverges]. Which blocks to copy is the caller's
+ * bookkeeping (paged_kv_cache_06_amd.blocks.plan_copy_on_write does it on the
+ * host); run the copies before the step's kv_append.
+ *
+ * src, dst: device int32 [num_pairs]. A pair with an id outside [0, N), or
+ * with src == dst, is skipped. No dst may appear twice or also be a src in
+ * the same call (the copies run concurrently; such a call has no defined
+ * result). k_pool, v_pool: 16-byte aligned, layouts as for kv_append. With
+ * num_layers > 1 the pools hold num_layers layers of N blocks each,
+ * layer_stride halves apart (a multiple of 8, at least N*Hkv*D*block_size),
+ * the same block ids in every layer, and every layer is copied; with
+ * num_layers == 1 layer_stride is ignored. num_pairs == 0 returns PA_OK.
+ */
+pa_status kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src, const int32_t *dst, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t num_layers, int64_t layer_stride, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -13,6 +13,7 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables,
                            seq_lens, block_size, scale, out=None,
                            workspace=None)   (the two calls above, fused)
+  kv_copy_blocks(k_pool, v_pool, src, dst, block_size)   (copy-on-write)
   paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                               block_size, max_blocks_per_seq)
@@ -65,6 +66,8 @@ def lib():
     L.paged_decode_attn.restype = ctypes.c_int
     L.paged_decode_attn_append.argtypes = [vp] * 8 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
     L.paged_decode_attn_append.restype = ctypes.c_int
+    L.kv_copy_blocks.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
+    L.kv_copy_blocks.restype = ctypes.c_int
     L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
     L.paged_gather_kv.restype = ctypes.c_int
     _lib = L
@@ -196,6 +199,27 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables, seq_
     )
     _check(st, "paged_decode_attn_append")
     return out
+
+
+def kv_copy_blocks(k_pool, v_pool, src, dst, block_size, stream=None):
+    """Block dst[i] <- block src[i] in both pools (copy-on-write); pools of one
+    layer ([N][Hkv][D/8][bs][8], [N][Hkv][D][bs]) or of several layers with a
+    leading layer dimension, every layer copied."""
+    layered = k_pool.dim() == 6
+    kp1 = k_pool[0] if layered else k_pool
+    vp1 = v_pool[0] if layered else v_pool
+    N, Hkv, D = _pool_dims(kp1, vp1, block_size)
+    layers = k_pool.shape[0] if layered else 1
+    if layered and (v_pool.dim() != 5 or v_pool.shape[0] != layers):
+        raise ValueError("k_pool / v_pool must both have the same leading layer dimension")
+    if tuple(src.shape) != tuple(dst.shape) or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D of the same length")
+    st = lib().kv_copy_blocks(
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(src, "src", torch.int32, 1), _dev(dst, "dst", torch.int32, 1),
+        src.numel(), Hkv, D, block_size, N, layers, ctypes.c_int64(N * Hkv * D * block_size), _stream(stream),
+    )
+    _check(st, "kv_copy_blocks")
 
 
 def paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size, k_out=None, v_out=None, stream=None):

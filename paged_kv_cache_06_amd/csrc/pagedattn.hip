@@ -955,6 +955,33 @@ __global__ void __launch_bounds__(256) gather_kernel(uint16_t* __restrict__ k_ou
     }
 }
 
+// Copy-on-write block copy: workgroup (pair, layer, pool) copies one block of
+// the K pool (z = 0) or the V pool (z = 1). A block is Hkv*D*bs contiguous
+// halves in both layouts; each thread moves eight 16-byte pieces per round
+// (a whole 32 KiB block at the Qwen shape), all loads in flight before the
+// stores, which are non-temporal: the copy is not read again by this launch.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int N,
+                                                          long long block_elems, long long layer_stride) {
+    const int s = src[blockIdx.x], t = dst[blockIdx.x];
+    if ((unsigned)s >= (unsigned)N || (unsigned)t >= (unsigned)N || s == t) return;
+    uint16_t* base = (blockIdx.z ? v_pool : k_pool) + (long long)blockIdx.y * layer_stride;
+    const u32x4* from = reinterpret_cast<const u32x4*>(base + (long long)s * block_elems);
+    u32x4* to = reinterpret_cast<u32x4*>(base + (long long)t * block_elems);
+    const int n16 = (int)(block_elems / 8);
+    constexpr int kU = 8;
+    for (int i0 = threadIdx.x; i0 < n16; i0 += 256 * kU) {
+        u32x4 x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (i0 + u * 256 < n16) x[u] = from[i0 + u * 256];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (i0 + u * 256 < n16) __builtin_nontemporal_store(x[u], &to[i0 + u * 256]);
+    }
+}
+
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0;
@@ -1215,6 +1242,23 @@ pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint1
     return launch_decode(out, q, k_pool, v_pool, block_tables, seq_lens, k_new, v_new, num_seqs, num_heads,
                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, workspace,
                          workspace_bytes, stream);
+}
+
+pa_status kv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t num_layers, int64_t layer_stride, void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 || block_size <= 0 || num_blocks <= 0 ||
+        num_layers <= 0 || num_layers > 65535)
+        return PA_ERR_INVALID_ARG;
+    const long long block_elems = (long long)num_kv_heads * head_dim * block_size;
+    if (num_layers > 1 && (layer_stride < block_elems * num_blocks || layer_stride % 8)) return PA_ERR_INVALID_ARG;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_pool || !v_pool || !src || !dst) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+    const long long stride = num_layers > 1 ? (long long)layer_stride : 0;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)num_layers, 2), dim3(256), 0,
+                       (hipStream_t)stream, k_pool, v_pool, src, dst, num_blocks, block_elems, stride);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status paged_gather_kv(uint16_t* k_out, uint16_t* v_out, const uint16_t* k_pool, const uint16_t* v_pool,

@@ -32,7 +32,8 @@ def pa():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_workspace_size",
-              "paged_decode_workspace_init", "paged_gather_kv", "pa_status_string", "paged_decode_supported"]:
+              "paged_decode_workspace_init", "kv_copy_blocks", "paged_gather_kv", "pa_status_string",
+              "paged_decode_supported"]:
         assert n in names
 
 
@@ -123,6 +124,25 @@ def test_fused_append_rejects_bad_arguments_on_host(pa):
     assert _decode_append(L, bs=24) == 2
     assert _decode_append(L, wsb=100) == 4
     assert _decode_append(L, B=0) == 0  # nothing to do
+
+
+def test_copy_blocks_rejects_bad_arguments_on_host(pa):
+    L = pa.lib()
+    f = FAKE
+    i64 = ctypes.c_int64
+
+    def cp(k=f, v=f, s=f, d=f, n=4, Hkv=2, D=128, bs=64, N=16, layers=1, stride=0):
+        return L.kv_copy_blocks(k, v, s, d, n, Hkv, D, bs, N, layers, i64(stride), None)
+
+    assert cp(n=-1) == 1
+    assert cp(D=100) == 1  # head_dim % 8
+    assert cp(N=0) == 1
+    assert cp(layers=0) == 1
+    assert cp(layers=2, stride=16 * 2 * 128 * 64 - 8) == 1  # layers would overlap
+    assert cp(layers=2, stride=16 * 2 * 128 * 64 + 4) == 1  # not 16-byte aligned
+    assert cp(s=None) == 1
+    assert cp(k=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned pool
+    assert cp(n=0) == 0  # nothing to do
 
 
 def test_append_and_gather_reject_bad_arguments_on_host(pa):
