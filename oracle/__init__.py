@@ -55,6 +55,8 @@ def _load(path=None):
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_kv_copy_blocks.argtypes = [u16p, u16p, i32p, i32p] + [i32] * 5
     lib.oracle_kv_copy_blocks.restype = ctypes.c_int
+    lib.oracle_kv_scatter_prefill.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 7
+    lib.oracle_kv_scatter_prefill.restype = ctypes.c_int
     lib.oracle_gather_kv.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
     lib.oracle_gather_kv.restype = ctypes.c_int
     lib.oracle_paged_decode_attn.argtypes = [f32p, u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 7 + [
@@ -130,6 +132,21 @@ class Oracle:
             self._p(kp, ctypes.c_uint16), self._p(vp, ctypes.c_uint16),
             self._p(s, ctypes.c_int32), self._p(d, ctypes.c_int32),
             s.size, Hkv, D, bs, N,
+        )
+
+    def kv_scatter_prefill(self, k_src, v_src, k_pool, v_pool, tables, prompt_lens, bs):
+        """In-place: row b's prompt (right-aligned in the [B][Hkv][S][D] group) into its blocks."""
+        B, Hkv, S, D = k_src.shape
+        W = tables.shape[1]
+        N = k_pool.shape[0]
+        kp, vp = k_pool.view(np.uint16), v_pool.view(np.uint16)
+        t = np.ascontiguousarray(tables, dtype=np.int32)
+        p = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+        return self.lib.oracle_kv_scatter_prefill(
+            self._p(self._bits(k_src), ctypes.c_uint16), self._p(self._bits(v_src), ctypes.c_uint16),
+            self._p(kp, ctypes.c_uint16), self._p(vp, ctypes.c_uint16),
+            self._p(t, ctypes.c_int32), self._p(p, ctypes.c_int32),
+            B, Hkv, D, bs, W, N, S,
         )
 
     def gather_kv(self, k_pool, v_pool, tables, seq_lens, bs, Hkv, D, fill=0):

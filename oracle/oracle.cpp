@@ -225,6 +225,45 @@ int oracle_kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src
     return rc;
 }
 
+// Scatter a prefill group's keys and values into the rows' blocks. The group
+// was run left padded to its widest prompt (width S), so row b's prompt of
+// length P = prompt_lens[b] sits at positions S-P .. S-1 of its [S][D] rows
+// of k_src / v_src ([B][Hkv][S][D]); its token t goes to block
+// block_tables[b][t / bs], slot t % bs, and the padding is dropped [Paged
+// attention, "What changed"]. A bit copy; slots past P and blocks no row
+// lists are untouched. Returns 0, -1 on bad dimensions, or -2 if a row's
+// length exceeds S or W*bs or it lists a block outside [0, N) (nothing more
+// of that row is written).
+int oracle_kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint16_t *k_pool, uint16_t *v_pool,
+                              const int32_t *block_tables, const int32_t *prompt_lens, int B, int Hkv, int D,
+                              int bs, int W, int N, int S) {
+    if (!dims_ok(B, Hkv, Hkv, D, bs, W) || N <= 0 || S <= 0) return -1;
+    int rc = 0;
+    for (int b = 0; b < B; ++b) {
+        const int P = prompt_lens[b];
+        if (P <= 0) continue;
+        if (P > S || (int64_t)P > (int64_t)W * bs) {
+            rc = -2;
+            continue;
+        }
+        for (int t = 0; t < P; ++t) {
+            const int32_t blk = block_tables[(size_t)b * W + t / bs];
+            if (blk < 0 || blk >= N) {
+                rc = -2;
+                break;
+            }
+            const size_t s = (size_t)(S - P + t);
+            for (int g = 0; g < Hkv; ++g)
+                for (int d = 0; d < D; ++d) {
+                    const size_t i = (((size_t)b * Hkv + g) * S + s) * D + d;
+                    k_pool[k_index(blk, g, t % bs, d, Hkv, D, bs)] = k_src[i];
+                    v_pool[v_index(blk, g, t % bs, d, Hkv, D, bs)] = v_src[i];
+                }
+        }
+    }
+    return rc;
+}
+
 // Copy each row's first seq_len tokens out of the pool into contiguous
 // [B][Hkv][W*bs][D] arrays, walking the table; positions >= seq_len are left
 // untouched. This is the "read the same blocks" debug path [Paged attention,

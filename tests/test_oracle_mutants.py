@@ -44,6 +44,9 @@ MUTANTS = {
     ),
     "copy_skips_last_slot": ("for (int slot = 0; slot < bs; ++slot)\n                for (int d = 0; d < D; ++d) {",
                              "for (int slot = 0; slot < bs - 1; ++slot)\n                for (int d = 0; d < D; ++d) {"),
+    "scatter_keeps_left_padding": ("const size_t s = (size_t)(S - P + t);", "const size_t s = (size_t)t;"),
+    "scatter_slot_off_by_one": ("k_pool[k_index(blk, g, t % bs, d, Hkv, D, bs)] = k_src[i];",
+                                "k_pool[k_index(blk, g, (t + 1) % bs, d, Hkv, D, bs)] = k_src[i];"),
     "copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)",
                              "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)"),
 }
@@ -63,6 +66,7 @@ FAST_PINS = [
     (pins.test_kv_append_matches_numpy_scatter, {"cfg": "tiny"}),
     (pins.test_kv_append_then_attention_sees_new_token, {}),
     (pins.test_kv_copy_blocks_matches_numpy, {"shape": (2, 128, 64)}),
+    (pins.test_kv_scatter_prefill_drops_the_left_padding, {}),
 ]
 
 

@@ -406,6 +406,38 @@ def test_kv_copy_blocks_matches_numpy(oracle, shape):
     assert np.array_equal(v3.view(np.uint16), ev.view(np.uint16))
 
 
+def test_kv_scatter_prefill_drops_the_left_padding(oracle):
+    # A left-padded prefill group's K/V: row b's prompt occupies the last P_b
+    # of the S positions. After the scatter, reading row b back through its
+    # table gives exactly those P_b positions, in order (numpy slicing and the
+    # workloads' own block reader, not the oracle), and no other slot moved.
+    rng = np.random.default_rng(83)
+    B, Hkv, D, bs, S = 5, 2, 64, 16, 70
+    lens = [70, 1, 16, 33, 0]
+    N = sum(wl.blocks_for(L, bs) for L in lens) + 6
+    w = wl.make_workload("pf", B, 4, Hkv, D, bs, N, lens, seed=84, events=12)
+    ld = w.layer(0)
+    k_src = wl.normal_f16(rng, (B, Hkv, S, D))
+    v_src = wl.normal_f16(rng, (B, Hkv, S, D))
+    kp, vp = ld.k_pool.copy(), ld.v_pool.copy()
+    assert oracle.kv_scatter_prefill(k_src, v_src, kp, vp, w.tables, w.seq_lens, bs) == 0
+    touched = np.zeros((N, bs), bool)
+    for b, P in enumerate(lens):
+        k, v = wl.read_row(kp, vp, w.tables[b], P, bs)  # [P][Hkv][D]
+        assert np.array_equal(k.view(np.uint16), k_src[b, :, S - P:, :].transpose(1, 0, 2).view(np.uint16))
+        assert np.array_equal(v.view(np.uint16), v_src[b, :, S - P:, :].transpose(1, 0, 2).view(np.uint16))
+        for t in range(P):
+            touched[w.tables[b, t // bs], t % bs] = True
+    kd = np.broadcast_to(~touched[:, None, None, :, None], kp.shape)
+    vd = np.broadcast_to(~touched[:, None, None, :], vp.shape)
+    assert np.array_equal(kp.view(np.uint16)[kd], ld.k_pool.view(np.uint16)[kd])
+    assert np.array_equal(vp.view(np.uint16)[vd], ld.v_pool.view(np.uint16)[vd])
+    # a prompt wider than the group is refused
+    bad = np.array(lens, np.int32)
+    bad[1] = S + 1
+    assert oracle.kv_scatter_prefill(k_src, v_src, ld.k_pool.copy(), ld.v_pool.copy(), w.tables, bad, bs) == -2
+
+
 def test_gather_matches_numpy(oracle):
     w = wl.make_workload("g", 5, 12, 2, 128, 16, 128, [0, 1, 16, 17, 300], seed=71, events=40)
     ld = w.layer(0)
