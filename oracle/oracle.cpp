@@ -232,8 +232,8 @@ int oracle_kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src
 // block_tables[b][t / bs], slot t % bs, and the padding is dropped [Paged
 // attention, "What changed"]. A bit copy; slots past P and blocks no row
 // lists are untouched. Returns 0, -1 on bad dimensions, or -2 if a row's
-// length exceeds S or W*bs or it lists a block outside [0, N) (nothing more
-// of that row is written).
+// length exceeds S or W*bs (the row is skipped) or it lists a block outside
+// [0, N) (that block's tokens are skipped).
 int oracle_kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint16_t *k_pool, uint16_t *v_pool,
                               const int32_t *block_tables, const int32_t *prompt_lens, int B, int Hkv, int D,
                               int bs, int W, int N, int S) {
@@ -250,7 +250,7 @@ int oracle_kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint
             const int32_t blk = block_tables[(size_t)b * W + t / bs];
             if (blk < 0 || blk >= N) {
                 rc = -2;
-                break;
+                continue;
             }
             const size_t s = (size_t)(S - P + t);
             for (int g = 0; g < Hkv; ++g)
