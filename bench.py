@@ -230,6 +230,67 @@ def bench_copy_blocks(args, torch, pa):
     print(json.dumps(line), flush=True)
 
 
+def bench_scatter_prefill(args, torch, pa):
+    """kv_scatter_prefill alone: a prefill group of 32 prompts of seeded
+    U{16..4096} tokens (the pages' range of prompt lengths), left padded to
+    4096, Qwen-shaped (2 KV heads, head_dim 128), block 64, scattered into
+    shuffled blocks of a 4,096-block pool; replicas rotated. Bytes per call:
+    every prompt token's K and V read once and written once."""
+    B, Hkv, D, bs, S = 32, 2, 128, 64, 4096
+    rng = np.random.default_rng(19)
+    prompts = rng.integers(16, S + 1, size=B).astype(np.int32)
+    w = wl.make_workload("scatter", B, 12, Hkv, D, bs, 4096, prompts, seed=19, events=0, append=False)
+    moved = int(prompts.sum()) * Hkv * D * 2 * 2 * 2
+    group_bytes = B * Hkv * S * D * 2 * 2
+    R = args.replicas or max(1, math.ceil((1 << 30) / (group_bytes + 4096 * Hkv * D * bs * 2 * 2)))
+    ks0 = torch.from_numpy(wl.normal_f16(rng, (B, Hkv, S, D))).cuda()
+    vs0 = torch.from_numpy(wl.normal_f16(rng, (B, Hkv, S, D))).cuda()
+    kp0 = torch.zeros(wl.k_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
+    vp0 = torch.zeros(wl.v_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
+    sets = [(ks0, vs0, kp0, vp0)] + [tuple(t.clone() for t in (ks0, vs0, kp0, vp0)) for _ in range(R - 1)]
+    tables = torch.from_numpy(w.tables).cuda()
+    plen = torch.from_numpy(prompts).cuda()
+    torch.cuda.synchronize()
+
+    def call(i):
+        ks, vs, kp, vp = sets[i % R]
+        pa.kv_scatter_prefill(ks, vs, kp, vp, tables, plen, bs)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        call(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = moved / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "kv_scatter_prefill (post-prefill scatter) achieved HBM GB/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "scatter_prefill", "rows": B, "padded_len": S, "prompt_tokens": int(prompts.sum()),
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs, "replicas": R, "bytes_per_call": moved},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "scatter_prefill_kernel",
+                     "bytes_per_launch": moved},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,8 +306,9 @@ def parse():
                     help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
     ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks"],
-                    help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone")
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill"],
+                    help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
+                         "scatter_prefill: the post-prefill scatter alone")
     ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
     return ap.parse_args()
 
@@ -278,6 +340,9 @@ def main():
     torch.cuda.set_device(0)
     if args.op == "copy_blocks":
         bench_copy_blocks(args, torch, pa)
+        return
+    if args.op == "scatter_prefill":
+        bench_scatter_prefill(args, torch, pa)
         return
     w = wl.CONFIGS[args.config]()
     layers = w.layers

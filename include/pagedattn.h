@@ -212,6 +212,30 @@ pa_status kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src,
                          int32_t num_layers, int64_t layer_stride, void *stream);
 
 /*
+ * kv_scatter_prefill -- after a prefill, move each row's prompt K/V into its
+ * blocks [Paged attention, "What changed": newly admitted requests are
+ * prefilled together, left padded to the group's widest prompt, and each
+ * row's KV is then copied into its blocks with the padding dropped].
+ *
+ * k_src, v_src: [num_seqs][Hkv][S][D] fp16 (S = padded_len, token-major rows
+ * of D channels), 16-byte aligned; row b's prompt of length P =
+ * prompt_lens[b] occupies positions S-P .. S-1. For t < P:
+ *     K[block_tables[b][t/bs]][g][d/8][t%bs][d%8] = k_src[b][g][S-P+t][d]
+ *     V[block_tables[b][t/bs]][g][d][t%bs]        = v_src[b][g][S-P+t][d]
+ * A bit copy; slots past P and unlisted blocks are untouched. Rows with P <= 0
+ * are skipped, and so are rows with P > S or P > W*block_size; a table entry
+ * outside [0, N) skips that block's tokens. Host checks: head_dim % 8 == 0,
+ * num_seqs and num_kv_heads <= 65535, block_size <= 1024, and the LDS
+ * transpose tile (max of D/8*(bs+1)*16 and D*(bs+8)*2 bytes) within 64 KiB,
+ * else PA_ERR_UNSUPPORTED. The tables must give each row private blocks for
+ * its prompt (no two rows writing one slot).
+ */
+pa_status kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint16_t *k_pool, uint16_t *v_pool,
+                             const int32_t *block_tables, const int32_t *prompt_lens, int32_t num_seqs,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t num_blocks, int32_t padded_len, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -14,6 +14,8 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
                            seq_lens, block_size, scale, out=None,
                            workspace=None)   (the two calls above, fused)
   kv_copy_blocks(k_pool, v_pool, src, dst, block_size)   (copy-on-write)
+  kv_scatter_prefill(k_src, v_src, k_pool, v_pool, block_tables,
+                     prompt_lens, block_size)            (after prefill)
   paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                               block_size, max_blocks_per_seq)
@@ -68,6 +70,8 @@ def lib():
     L.paged_decode_attn_append.restype = ctypes.c_int
     L.kv_copy_blocks.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
     L.kv_copy_blocks.restype = ctypes.c_int
+    L.kv_scatter_prefill.argtypes = [vp] * 6 + [i32] * 7 + [vp]
+    L.kv_scatter_prefill.restype = ctypes.c_int
     L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
     L.paged_gather_kv.restype = ctypes.c_int
     _lib = L
@@ -220,6 +224,27 @@ def kv_copy_blocks(k_pool, v_pool, src, dst, block_size, stream=None):
         src.numel(), Hkv, D, block_size, N, layers, ctypes.c_int64(N * Hkv * D * block_size), _stream(stream),
     )
     _check(st, "kv_copy_blocks")
+
+
+def kv_scatter_prefill(k_src, v_src, k_pool, v_pool, block_tables, prompt_lens, block_size, stream=None):
+    """Row b's prompt KV (the last prompt_lens[b] of the S positions of a
+    left-padded prefill group, k_src / v_src [B][Hkv][S][D]) into its blocks,
+    padding dropped."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, W = block_tables.shape
+    if k_src.dim() != 4 or tuple(k_src.shape[:2]) != (B, Hkv) or k_src.shape[3] != D:
+        raise ValueError("k_src must be [B][Hkv][S][D]")
+    if tuple(v_src.shape) != tuple(k_src.shape):
+        raise ValueError("v_src must have k_src's shape")
+    if tuple(prompt_lens.shape) != (B,):
+        raise ValueError("prompt_lens must be [B]")
+    st = lib().kv_scatter_prefill(
+        _dev(k_src, "k_src", torch.float16, 4), _dev(v_src, "v_src", torch.float16, 4),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(prompt_lens, "prompt_lens", torch.int32, 1),
+        B, Hkv, D, block_size, W, N, k_src.shape[2], _stream(stream),
+    )
+    _check(st, "kv_scatter_prefill")
 
 
 def paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size, k_out=None, v_out=None, stream=None):

@@ -982,6 +982,75 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(uint16_t* __restrict__
     }
 }
 
+// Post-prefill scatter: workgroup (x, KV head g, row b) moves the keys (x < W:
+// logical block j = x) or the values (x >= W: j = x - W) of the row's tokens
+// j*bs .. j*bs+bs-1 from the left-padded prefill group
+// ([B][Hkv][S][D], token-major; row b's prompt right-aligned) into physical
+// block block_tables[b][j]. Both pool layouts want a transpose of the
+// token-major source (K: [D/8][bs][8], V: [D][bs]), done through LDS so that
+// the global reads run along the channels and the writes along the slots:
+// K in 16-byte units (row stride bs+1 units, conflict-free), then V in halves
+// (row stride bs+8 halves), the writes 16 bytes per lane where eight whole
+// slots are present and 2 bytes per slot at a partial end; the 16-byte writes
+// are non-temporal (nothing in this launch reads them).
+__global__ void __launch_bounds__(256) scatter_prefill_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, uint16_t* __restrict__ k_pool,
+    uint16_t* __restrict__ v_pool, const int32_t* __restrict__ tables, const int32_t* __restrict__ prompt_lens,
+    int Hkv, int D, int BS, int W, int N, int S) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+    const bool vpart = (int)blockIdx.x >= W;
+    const int j = vpart ? blockIdx.x - W : blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int P = prompt_lens[b];
+    const int t0 = j * BS;
+    if (P <= 0 || P > S || (long long)P > (long long)W * BS || t0 >= P) return;
+    const int blk = tables[(size_t)b * W + j];
+    if ((unsigned)blk >= (unsigned)N) return;
+    const int n = min(BS, P - t0);  // tokens of this block
+    const int C = D / 8;             // 16-byte channel groups per token
+    const size_t src0 = (((size_t)b * Hkv + g) * S + (size_t)(S - P + t0)) * D;  // the block's first token
+    const size_t dst0 = ((size_t)blk * Hkv + g) * (size_t)D * BS;             // the (block, head) slab, both pools
+
+    if (!vpart) {  // ---- K: [token][D] -> [D/8][bs][8]
+        u32x4* sk = reinterpret_cast<u32x4*>(s_raw);  // [C][BS + 1]
+        for (int u = threadIdx.x; u < n * C; u += 256) {
+            const int i = u / C, c = u - i * C;
+            sk[c * (BS + 1) + i] = *reinterpret_cast<const u32x4*>(k_src + src0 + (size_t)i * D + 8 * c);
+        }
+        __syncthreads();
+        for (int u = threadIdx.x; u < n * C; u += 256) {
+            const int c = u / n, i = u - c * n;
+            __builtin_nontemporal_store(sk[c * (BS + 1) + i], reinterpret_cast<u32x4*>(k_pool + dst0 + ((size_t)c * BS + i) * 8));
+        }
+        return;
+    }
+
+    // ---- V: [token][D] -> [D][bs]
+    uint16_t* sv = reinterpret_cast<uint16_t*>(s_raw);  // [D][BS + 8]
+    const int R = BS + 8;
+    for (int u = threadIdx.x; u < n * C; u += 256) {
+        const int i = u / C, c = u - i * C;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(v_src + src0 + (size_t)i * D + 8 * c);
+        const unsigned w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sv[(8 * c + 2 * k) * R + i] = (uint16_t)(w4[k] & 0xffffu);
+            sv[(8 * c + 2 * k + 1) * R + i] = (uint16_t)(w4[k] >> 16);
+        }
+    }
+    __syncthreads();
+    const int n8 = (BS % 8 == 0) ? n / 8 : 0;  // whole 8-slot groups (16-byte aligned in the pool)
+    for (int u = threadIdx.x; u < D * n8; u += 256) {
+        const int d = u / n8, q = u - d * n8;
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sv + d * R + 8 * q),
+                                    reinterpret_cast<u32x4*>(v_pool + dst0 + (size_t)d * BS + 8 * q));
+    }
+    const int rest = n - 8 * n8;  // slots past the last whole group
+    for (int u = threadIdx.x; u < D * rest; u += 256) {
+        const int d = u / rest, i = 8 * n8 + (u - d * rest);
+        v_pool[dst0 + (size_t)d * BS + i] = sv[d * R + i];
+    }
+}
+
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0;
@@ -1258,6 +1327,29 @@ pa_status kv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src,
     const long long stride = num_layers > 1 ? (long long)layer_stride : 0;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)num_layers, 2), dim3(256), 0,
                        (hipStream_t)stream, k_pool, v_pool, src, dst, num_blocks, block_elems, stride);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status kv_scatter_prefill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
+                             const int32_t* block_tables, const int32_t* prompt_lens, int32_t num_seqs,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t num_blocks, int32_t padded_len, void* stream) {
+    if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 || head_dim <= 0 ||
+        head_dim % 8 || block_size <= 0 || block_size > 1024 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+        padded_len <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_src || !v_src || !k_pool || !v_pool || !block_tables || !prompt_lens) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+    // LDS: the larger of the K tile ([D/8][bs+1] x 16 B) and the V tile ([D][bs+8] x 2 B)
+    const size_t lds = std::max<size_t>((size_t)(head_dim / 8) * (block_size + 1) * 16,
+                                        (size_t)head_dim * (block_size + 8) * 2);
+    if (lds > 64 * 1024) return PA_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * 2 > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(scatter_prefill_kernel, dim3((unsigned)max_blocks_per_seq * 2, (unsigned)num_kv_heads,
+                                                    (unsigned)num_seqs),
+                       dim3(256), lds, (hipStream_t)stream, k_src, v_src, k_pool, v_pool, block_tables, prompt_lens,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, padded_len);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -32,7 +32,8 @@ def pa():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_workspace_size",
-              "paged_decode_workspace_init", "kv_copy_blocks", "paged_gather_kv", "pa_status_string",
+              "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
+              "pa_status_string",
               "paged_decode_supported"]:
         assert n in names
 
@@ -143,6 +144,23 @@ def test_copy_blocks_rejects_bad_arguments_on_host(pa):
     assert cp(s=None) == 1
     assert cp(k=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned pool
     assert cp(n=0) == 0  # nothing to do
+
+
+def test_scatter_prefill_rejects_bad_arguments_on_host(pa):
+    L = pa.lib()
+    f = FAKE
+
+    def sc(ks=f, vs=f, k=f, v=f, t=f, p=f, B=4, Hkv=2, D=128, bs=64, W=4, N=16, S=300):
+        return L.kv_scatter_prefill(ks, vs, k, v, t, p, B, Hkv, D, bs, W, N, S, None)
+
+    assert sc(D=100) == 1
+    assert sc(S=0) == 1
+    assert sc(bs=0) == 1
+    assert sc(bs=2048) == 1
+    assert sc(p=None) == 1
+    assert sc(ks=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned source
+    assert sc(D=512, bs=128) == 2  # transpose tile beyond 64 KiB of LDS
+    assert sc(B=0) == 0
 
 
 def test_append_and_gather_reject_bad_arguments_on_host(pa):
