@@ -7,7 +7,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "pagedattn.hip")
+SRC = os.path.join(HERE, "csrc", "pagedattn.hip")  # decode attention
+SOURCES = [SRC, os.path.join(HERE, "csrc", "blockops.hip")]  # and the block operations
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpagedattn.so")
 
@@ -30,7 +31,7 @@ def hipcc() -> str:
 
 def build(out: str = LIB, extra=()) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, *SOURCES, "-o", tmp]
     subprocess.run(cmd, check=True, stderr=subprocess.PIPE)
     os.replace(tmp, out)
     return out

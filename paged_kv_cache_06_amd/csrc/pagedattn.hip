@@ -1,53 +1,25 @@
-// libpagedattn: paged KV-cache decode attention for MI355X (gfx950).
+// libpagedattn, decode attention: paged KV-cache decode attention for MI355X
+// (gfx950). The block operations (kv_append, kv_copy_blocks,
+// kv_scatter_prefill, paged_gather_kv) live in blockops.hip; both files build
+// into one library behind the C ABI of include/pagedattn.h.
 //
 // Sources (page title, section):
 //   [Paged attention]     danielfleming.xyz/writing/inference/paged
 //   [PagedAttention]      deepconcepts.dev/c/llm-paged-attention
 //   [SLM paged attention] aicassindra.com/blogs/slm/slm_paged_attention.html
 //
-// Three kernels sit behind the C ABI declared in include/pagedattn.h:
-//
-//   append_kernel   one decode step's K/V scattered into each row's last block
-//                   [SLM paged attention, "End-to-end flow"].
-//   decode_kernel   one query token per row; the row's table is walked, its
-//                   blocks gathered at its own length [Paged attention, "What
-//                   changed"], and softmax attention computed for the query
-//                   heads of one KV group at once.
-//   gather_kernel   debug path: the same blocks copied out contiguously.
-//
-// decode_kernel design (CDNA4: 64-lane waves, 4 SIMDs per CU, fp16 dot2 on
-// the vector ALU, no matrix cores -- decode attention is a matrix-vector
-// product per KV group and HBM-bound):
-//
-//  * Work item = (row b, KV head g, partition p). A row's tokens are cut into
-//    64-token tiles; a partition is `chunk` consecutive tiles. Every
-//    workgroup reads seq_lens, sizes `chunk` so the launch yields about
-//    `target_wgs` items, and finds its own item by prefix sum -- no host
-//    sync, no empty work for short rows. The split over the sequence is exact
-//    because partial softmax results are rescaled and combined exactly
-//    [PagedAttention, "Sharing is the part that pays twice"].
-//  * A workgroup is 4 waves; wave w takes tiles w, w+4, ... of the
-//    partition. Per tile every lane issues 16-byte loads: with the K pool
-//    in [D/8][bs][8] order, load j of lane l is the 8 channels 8j..8j+7 of
-//    token l, so one load instruction covers 1 KiB of contiguous K and a
-//    lane ends up owning one token's whole key. With V in [D][bs] order,
-//    load jj of lane l is 8 consecutive tokens (8*(l%8)..) of channel row
-//    8*jj' + l/8, again 1 KiB contiguous per instruction.
-//  * QK: lane = token, dot products with v_dot2_f32_f16 against the query
-//    heads of the group (the same query bits for every lane, read through the
-//    scalar unit), so no cross-lane reduction is needed for scores.
-//  * Online softmax per tile: wave max by DPP row permutes plus the gfx950
-//    permlane16/32 swaps; p = exp2(s*scale*log2e - m) rounded to fp16 and
-//    passed through LDS to the V layout; l accumulated per lane.
-//  * PV: lane (l%8 = token chunk, l/8 = channel offset) accumulates
-//    p[t..t+7] . v[d][t..t+7] with dot2 into fp32 accumulators that persist
-//    across tiles. The V rows a lane loads are permuted (jj' = jj ^ f(l%8))
-//    so that the final reduction over the 8 lanes sharing a channel row is a
-//    transposing butterfly costing one DPP add per output.
-//  * The 4 waves merge through LDS; a one-partition row writes fp16 output
-//    directly. Otherwise the partition writes (max, sum, unnormalised
-//    output) to the workspace, and the last partition to arrive (atomic
-//    ticket) merges all of them in partition order, then resets the ticket.
+// decode_kernel: one query token per row; the row's block table is walked,
+// its blocks gathered at its own length [Paged attention, "What changed";
+// PagedAttention, "What the block table costs"], and softmax attention
+// computed for the query heads of one KV group at once; long rows are split
+// over workgroups and their partial results merged exactly [PagedAttention,
+// "Sharing is the part that pays twice"]. With k_new / v_new it also performs
+// the step's kv_append [SLM paged attention, "End-to-end flow"]. It runs on
+// the vector ALU (fp16 dot2 with fp32 accumulation): decode attention is a
+// matrix-vector product per KV group, bound by HBM bandwidth, so no matrix
+// cores. The design (persistent workgroups over balanced tile ranges, a load
+// wave issuing direct-to-LDS loads, compute waves per two query heads, the
+// merge by the last partition to arrive) is described above decode_kernel.
 //
 // Stale slots and unlisted blocks may hold NaN: scores of tokens past the
 // row's length are replaced (not multiplied) by -inf, and their V halves are
@@ -876,180 +848,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// kv_append, gather, workspace fill
+// workspace fill
 // ---------------------------------------------------------------------------
-
-// One wave per (row, KV head): lanes 0..D/8-1 copy the 16-byte K groups,
-// every lane copies D/64 (or fewer) V channels. The new token's K and V are
-// requested before the row's length and table entry, which they do not depend
-// on, so the call costs two dependent memory round trips instead of three.
-__global__ void __launch_bounds__(64) append_kernel(const uint16_t* __restrict__ k_new,
-                                                    const uint16_t* __restrict__ v_new,
-                                                    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
-                                                    const int32_t* __restrict__ tables,
-                                                    const int32_t* __restrict__ seq_lens, int Hkv, int D, int BS,
-                                                    int W, int N) {
-    constexpr int kMaxV = 8;  // V channels per lane held in registers (D <= 512)
-    const int bg = blockIdx.x;
-    const int b = bg / Hkv, g = bg % Hkv;
-    const int lane = threadIdx.x;
-    const uint16_t* ksrc = k_new + ((size_t)b * Hkv + g) * D;
-    const uint16_t* vsrc = v_new + ((size_t)b * Hkv + g) * D;
-    const bool fast = D <= 64 * kMaxV;
-    // Issued from assembly, at clamped (always valid) addresses, so that the
-    // compiler neither sinks them below the length and table reads nor waits
-    // for them early; the wait comes right before the stores.
-    u32x4 kx;
-    unsigned vx[kMaxV];
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kx) : "v"(ksrc + 8 * min(lane, D / 8 - 1)) : "memory");
-#pragma unroll
-    for (int i = 0; i < kMaxV; ++i)
-        asm volatile("global_load_ushort %0, %1, off" : "=v"(vx[i]) : "v"(vsrc + min(lane + 64 * i, D - 1)) : "memory");
-    const int L = seq_lens[b];
-    const bool live = L >= 1 && (long long)L <= (long long)W * BS;
-    const int pos = live ? L - 1 : 0;
-    const int blk = tables[(size_t)b * W + pos / BS];
-    asm volatile("s_waitcnt vmcnt(0)"  // the loads above have landed (also before leaving early)
-                 : "+v"(kx), "+v"(vx[0]), "+v"(vx[1]), "+v"(vx[2]), "+v"(vx[3]), "+v"(vx[4]), "+v"(vx[5]),
-                   "+v"(vx[6]), "+v"(vx[7])::"memory");
-    if (!live || blk < 0 || blk >= N) return;
-    const int slot = pos % BS;
-    const size_t base = (size_t)blk * Hkv + g;
-    if (fast) {
-        if (lane < D / 8) *reinterpret_cast<u32x4*>(k_pool + ((base * (D / 8) + lane) * BS + slot) * 8) = kx;
-#pragma unroll
-        for (int i = 0; i < kMaxV; ++i)
-            if (lane + 64 * i < D) v_pool[(base * D + lane + 64 * i) * BS + slot] = (uint16_t)vx[i];
-        return;
-    }
-    for (int j = lane; j < D / 8; j += 64) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(ksrc + 8 * j);
-        *reinterpret_cast<u32x4*>(k_pool + ((base * (D / 8) + j) * BS + slot) * 8) = x;
-    }
-    for (int d = lane; d < D; d += 64) v_pool[(base * D + d) * BS + slot] = vsrc[d];
-}
-
-// One workgroup per (row, KV head, logical block); thread per (token, channel).
-__global__ void __launch_bounds__(256) gather_kernel(uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
-                                                     const uint16_t* __restrict__ k_pool,
-                                                     const uint16_t* __restrict__ v_pool,
-                                                     const int32_t* __restrict__ tables,
-                                                     const int32_t* __restrict__ seq_lens, int Hkv, int D, int BS,
-                                                     int W, int N) {
-    const int j = blockIdx.x % W;
-    const int bg = blockIdx.x / W;
-    const int b = bg / Hkv, g = bg % Hkv;
-    const int cap = W * BS;
-    int L = seq_lens[b];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int t_lo = j * BS;
-    if (t_lo >= L) return;
-    const int n = min(BS, L - t_lo);
-    const int blk = clamp_block(tables[(size_t)b * W + j], N);
-    const size_t base = (size_t)blk * Hkv + g;
-    for (int e = threadIdx.x; e < n * D; e += blockDim.x) {
-        const int t = e / D, d = e % D;
-        const size_t o = (((size_t)bg * cap) + t_lo + t) * D + d;
-        k_out[o] = k_pool[((base * (D / 8) + d / 8) * BS + t) * 8 + d % 8];
-        v_out[o] = v_pool[(base * D + d) * BS + t];
-    }
-}
-
-// Copy-on-write block copy: workgroup (pair, layer, pool) copies one block of
-// the K pool (z = 0) or the V pool (z = 1). A block is Hkv*D*bs contiguous
-// halves in both layouts; each thread moves eight 16-byte pieces per round
-// (a whole 32 KiB block at the Qwen shape), all loads in flight before the
-// stores, which are non-temporal: the copy is not read again by this launch.
-__global__ void __launch_bounds__(256) copy_blocks_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
-                                                          const int32_t* __restrict__ src,
-                                                          const int32_t* __restrict__ dst, int N,
-                                                          long long block_elems, long long layer_stride) {
-    const int s = src[blockIdx.x], t = dst[blockIdx.x];
-    if ((unsigned)s >= (unsigned)N || (unsigned)t >= (unsigned)N || s == t) return;
-    uint16_t* base = (blockIdx.z ? v_pool : k_pool) + (long long)blockIdx.y * layer_stride;
-    const u32x4* from = reinterpret_cast<const u32x4*>(base + (long long)s * block_elems);
-    u32x4* to = reinterpret_cast<u32x4*>(base + (long long)t * block_elems);
-    const int n16 = (int)(block_elems / 8);
-    constexpr int kU = 8;
-    for (int i0 = threadIdx.x; i0 < n16; i0 += 256 * kU) {
-        u32x4 x[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-            if (i0 + u * 256 < n16) x[u] = from[i0 + u * 256];
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-            if (i0 + u * 256 < n16) __builtin_nontemporal_store(x[u], &to[i0 + u * 256]);
-    }
-}
-
-// Post-prefill scatter: workgroup (x, KV head g, row b) moves the keys (x < W:
-// logical block j = x) or the values (x >= W: j = x - W) of the row's tokens
-// j*bs .. j*bs+bs-1 from the left-padded prefill group
-// ([B][Hkv][S][D], token-major; row b's prompt right-aligned) into physical
-// block block_tables[b][j]. Both pool layouts want a transpose of the
-// token-major source (K: [D/8][bs][8], V: [D][bs]), done through LDS so that
-// the global reads run along the channels and the writes along the slots:
-// K in 16-byte units (row stride bs+1 units, conflict-free), then V in halves
-// (row stride bs+8 halves), the writes 16 bytes per lane where eight whole
-// slots are present and 2 bytes per slot at a partial end; the 16-byte writes
-// are non-temporal (nothing in this launch reads them).
-__global__ void __launch_bounds__(256) scatter_prefill_kernel(
-    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, uint16_t* __restrict__ k_pool,
-    uint16_t* __restrict__ v_pool, const int32_t* __restrict__ tables, const int32_t* __restrict__ prompt_lens,
-    int Hkv, int D, int BS, int W, int N, int S) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
-    const bool vpart = (int)blockIdx.x >= W;
-    const int j = vpart ? blockIdx.x - W : blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int P = prompt_lens[b];
-    const int t0 = j * BS;
-    if (P <= 0 || P > S || (long long)P > (long long)W * BS || t0 >= P) return;
-    const int blk = tables[(size_t)b * W + j];
-    if ((unsigned)blk >= (unsigned)N) return;
-    const int n = min(BS, P - t0);  // tokens of this block
-    const int C = D / 8;             // 16-byte channel groups per token
-    const size_t src0 = (((size_t)b * Hkv + g) * S + (size_t)(S - P + t0)) * D;  // the block's first token
-    const size_t dst0 = ((size_t)blk * Hkv + g) * (size_t)D * BS;             // the (block, head) slab, both pools
-
-    if (!vpart) {  // ---- K: [token][D] -> [D/8][bs][8]
-        u32x4* sk = reinterpret_cast<u32x4*>(s_raw);  // [C][BS + 1]
-        for (int u = threadIdx.x; u < n * C; u += 256) {
-            const int i = u / C, c = u - i * C;
-            sk[c * (BS + 1) + i] = *reinterpret_cast<const u32x4*>(k_src + src0 + (size_t)i * D + 8 * c);
-        }
-        __syncthreads();
-        for (int u = threadIdx.x; u < n * C; u += 256) {
-            const int c = u / n, i = u - c * n;
-            __builtin_nontemporal_store(sk[c * (BS + 1) + i], reinterpret_cast<u32x4*>(k_pool + dst0 + ((size_t)c * BS + i) * 8));
-        }
-        return;
-    }
-
-    // ---- V: [token][D] -> [D][bs]
-    uint16_t* sv = reinterpret_cast<uint16_t*>(s_raw);  // [D][BS + 8]
-    const int R = BS + 8;
-    for (int u = threadIdx.x; u < n * C; u += 256) {
-        const int i = u / C, c = u - i * C;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(v_src + src0 + (size_t)i * D + 8 * c);
-        const unsigned w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sv[(8 * c + 2 * k) * R + i] = (uint16_t)(w4[k] & 0xffffu);
-            sv[(8 * c + 2 * k + 1) * R + i] = (uint16_t)(w4[k] >> 16);
-        }
-    }
-    __syncthreads();
-    const int n8 = (BS % 8 == 0) ? n / 8 : 0;  // whole 8-slot groups (16-byte aligned in the pool)
-    for (int u = threadIdx.x; u < D * n8; u += 256) {
-        const int d = u / n8, q = u - d * n8;
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sv + d * R + 8 * q),
-                                    reinterpret_cast<u32x4*>(v_pool + dst0 + (size_t)d * BS + 8 * q));
-    }
-    const int rest = n - 8 * n8;  // slots past the last whole group
-    for (int u = threadIdx.x; u < D * rest; u += 256) {
-        const int d = u / rest, i = 8 * n8 + (u - d * rest);
-        v_pool[dst0 + (size_t)d * BS + i] = sv[d * R + i];
-    }
-}
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -1191,24 +991,6 @@ int paged_decode_supported(int32_t num_heads, int32_t num_kv_heads, int32_t head
     return pick_decode(block_size, head_dim, num_heads / num_kv_heads).fn != nullptr;
 }
 
-pa_status kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
-                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
-                    void* stream) {
-    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 || block_size <= 0 ||
-        max_blocks_per_seq <= 0 || num_blocks <= 0)
-        return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;
-    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
-        return PA_ERR_INVALID_ARG;
-    if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(append_kernel, dim3(num_seqs * num_kv_heads), dim3(64), 0, (hipStream_t)stream, k_new,
-                       v_new, k_pool, v_pool, block_tables, seq_lens, num_kv_heads, head_dim, block_size,
-                       max_blocks_per_seq, num_blocks);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block_size, int32_t max_blocks_per_seq) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
@@ -1311,63 +1093,6 @@ pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint1
     return launch_decode(out, q, k_pool, v_pool, block_tables, seq_lens, k_new, v_new, num_seqs, num_heads,
                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, workspace,
                          workspace_bytes, stream);
-}
-
-pa_status kv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, const int32_t* dst, int32_t num_pairs,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                         int32_t num_layers, int64_t layer_stride, void* stream) {
-    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 || block_size <= 0 || num_blocks <= 0 ||
-        num_layers <= 0 || num_layers > 65535)
-        return PA_ERR_INVALID_ARG;
-    const long long block_elems = (long long)num_kv_heads * head_dim * block_size;
-    if (num_layers > 1 && (layer_stride < block_elems * num_blocks || layer_stride % 8)) return PA_ERR_INVALID_ARG;
-    if (num_pairs == 0) return PA_OK;
-    if (!k_pool || !v_pool || !src || !dst) return PA_ERR_INVALID_ARG;
-    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
-    const long long stride = num_layers > 1 ? (long long)layer_stride : 0;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)num_layers, 2), dim3(256), 0,
-                       (hipStream_t)stream, k_pool, v_pool, src, dst, num_blocks, block_elems, stride);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
-pa_status kv_scatter_prefill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
-                             const int32_t* block_tables, const int32_t* prompt_lens, int32_t num_seqs,
-                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                             int32_t num_blocks, int32_t padded_len, void* stream) {
-    if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 || head_dim <= 0 ||
-        head_dim % 8 || block_size <= 0 || block_size > 1024 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
-        padded_len <= 0)
-        return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;
-    if (!k_src || !v_src || !k_pool || !v_pool || !block_tables || !prompt_lens) return PA_ERR_INVALID_ARG;
-    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
-    // LDS: the larger of the K tile ([D/8][bs+1] x 16 B) and the V tile ([D][bs+8] x 2 B)
-    const size_t lds = std::max<size_t>((size_t)(head_dim / 8) * (block_size + 1) * 16,
-                                        (size_t)head_dim * (block_size + 8) * 2);
-    if (lds > 64 * 1024) return PA_ERR_UNSUPPORTED;
-    if ((long long)max_blocks_per_seq * 2 > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(scatter_prefill_kernel, dim3((unsigned)max_blocks_per_seq * 2, (unsigned)num_kv_heads,
-                                                    (unsigned)num_seqs),
-                       dim3(256), lds, (hipStream_t)stream, k_src, v_src, k_pool, v_pool, block_tables, prompt_lens,
-                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, padded_len);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
-pa_status paged_gather_kv(uint16_t* k_out, uint16_t* v_out, const uint16_t* k_pool, const uint16_t* v_pool,
-                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
-                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                          int32_t num_blocks, void* stream) {
-    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 || block_size <= 0 ||
-        max_blocks_per_seq <= 0 || num_blocks <= 0)
-        return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;
-    if (!k_out || !v_out || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
-    const long long grid = (long long)num_seqs * num_kv_heads * max_blocks_per_seq;
-    if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, k_out, v_out, k_pool,
-                       v_pool, block_tables, seq_lens, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                       num_blocks);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // extern "C"
