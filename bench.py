@@ -291,6 +291,95 @@ def bench_scatter_prefill(args, torch, pa):
     print(json.dumps(line), flush=True)
 
 
+def bench_contrast(args, torch, pa):
+    """The mixed batch (31 rows of U{16..512} tokens and one of 4,352) decoded
+    (a) paged, blocks shuffled through the pool (the normal path); (b) on the
+    contiguous layout (identity tables); (c) the way the earlier fixed-width
+    engine computed it: every row over the widest row's 4,352 positions,
+    masked (paged_decode_attn_masked on the contiguous layout); (d) paged at
+    block sizes 16, 32, 64, 128 and 256 with the same lengths. Decode kernel
+    duration per call from back-to-back launches; replicas rotated."""
+    w0 = wl.mixed()
+    lens = w0.seq_lens
+    B, Hq, Hkv, D = w0.B, w0.Hq, w0.Hkv, w0.D
+    width = int(lens.max())
+    kv_true = int(lens.sum()) * Hkv * D * 2 * 2
+    rng = np.random.default_rng(23)
+
+    def timed(name, make_call, touched):
+        R = min(32, max(1, math.ceil((1 << 30) / touched)))
+        first = make_call(None)
+        calls = [first] + [make_call(first) for _ in range(R - 1)]
+        for i in range(args.warmup):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            calls[i % R]()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / args.steps * 1e3
+        print(f"[contrast] {name}: {us:.2f} us per call ({R} replicas)", file=sys.stderr, flush=True)
+        return us, R
+
+    def setup(bs, tables, N, width_arg, like=None):
+        # random data once per configuration; further replicas are device copies of it
+        if like is None:
+            q = torch.from_numpy(wl.normal_f16(rng, (B, Hq, D))).cuda()
+            kp = torch.from_numpy(wl.normal_f16(rng, wl.k_pool_shape(N, Hkv, D, bs))).cuda()
+            vp = torch.from_numpy(wl.normal_f16(rng, wl.v_pool_shape(N, Hkv, D, bs))).cuda()
+        else:
+            q, kp, vp = (t.clone() for t in like.tensors)
+        tt = torch.from_numpy(tables).cuda()
+        ll = torch.from_numpy(lens).cuda()
+        ws = pa.new_workspace(B, Hq, Hkv, D, bs, tables.shape[1])
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+        if width_arg:
+            def call():
+                pa.paged_decode_attn_masked(q, kp, vp, tt, ll, bs, w0.scale, width_arg, out=out, workspace=ws)
+        else:
+            def call():
+                pa.paged_decode_attn(q, kp, vp, tt, ll, bs, w0.scale, out=out, workspace=ws)
+        call.tensors = (q, kp, vp)
+        return call
+
+    res = {}
+    bs = w0.bs
+    W = -(-width // bs)
+    ident = (np.arange(B, dtype=np.int32)[:, None] * W + np.arange(W, dtype=np.int32)[None, :]).astype(np.int32)
+    res["paged_us"], _ = timed("paged", lambda like: setup(bs, w0.tables, w0.N, 0, like), kv_true)
+    res["contiguous_us"], _ = timed("contiguous", lambda like: setup(bs, ident, B * W, 0, like), kv_true)
+    res["masked_width_us"], _ = timed("masked width", lambda like: setup(bs, ident, B * W, width, like),
+                                      B * width * Hkv * D * 4)
+    for b2 in (16, 32, 64, 128, 256):
+        nb = int(sum(-(-int(L) // b2) for L in lens))
+        w2 = wl.make_workload(f"mixed bs{b2}", B, Hq, Hkv, D, b2, nb + 64, lens, seed=3, events=200, append=False)
+        res[f"paged_bs{b2}_us"], _ = timed(f"paged bs {b2}", lambda like: setup(b2, w2.tables, w2.N, 0, like),
+                                           kv_true)
+    res = {k: round(v, 3) for k, v in res.items()}
+    line = {
+        "metric": "mixed-batch decode: width and gather contrasts (kernel us per call)",
+        "value": res["paged_us"],
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "mixed", "batch": B, "width": width, "true_tokens": int(lens.sum()),
+                   "kv_bytes_true": kv_true, "kv_bytes_masked_width": B * width * Hkv * D * 4},
+        "contrast": res,
+        "width_penalty": round(res["masked_width_us"] / res["contiguous_us"], 2),
+        "gather_penalty": round(res["paged_us"] / res["contiguous_us"], 3),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,9 +395,10 @@ def parse():
                     help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
     ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill"],
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
-                         "scatter_prefill: the post-prefill scatter alone")
+                         "scatter_prefill: the post-prefill scatter alone; contrast: the mixed batch decoded "
+                         "paged, contiguous, at masked full width, and at block sizes 16..256")
     ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
     return ap.parse_args()
 
@@ -343,6 +433,9 @@ def main():
         return
     if args.op == "scatter_prefill":
         bench_scatter_prefill(args, torch, pa)
+        return
+    if args.op == "contrast":
+        bench_contrast(args, torch, pa)
         return
     w = wl.CONFIGS[args.config]()
     layers = w.layers

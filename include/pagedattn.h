@@ -82,7 +82,7 @@ typedef enum {
 const char *pa_status_string(int status);
 
 /* 1 if paged_decode_attn has a kernel for this shape, else 0.
- * Compiled in: block_size in {16, 32, 64, 128}, head_dim in {64, 128},
+ * Compiled in: block_size in {16, 32, 64, 128, 256}, head_dim in {64, 128},
  * num_heads / num_kv_heads in {1, 2, 4, 6, 8}. */
 int paged_decode_supported(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size);
 
@@ -185,6 +185,28 @@ pa_status paged_decode_attn_append(uint16_t *out, const uint16_t *q, const uint1
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * paged_decode_attn_masked -- the contrast of the earlier contiguous engine:
+ * the same result as paged_decode_attn, computed the way a cache of one
+ * fixed-width slot per row computes it [Paged attention, "What changed": the
+ * earlier engine reserved the widest row's width for every row and masked
+ * the unused columns, which hid the data but not the work; Continuous
+ * batching, "What changed": a mask tells the decode which cache columns
+ * belong to which row]. Every
+ * row with seq_lens[b] >= 1 reads and scores max(width, seq_lens[b]) tokens
+ * (its table must list that many tokens' worth of valid blocks), and positions at or past
+ * seq_lens[b] are masked out of the softmax and the output. With an identity
+ * table (row b's blocks b*W .. b*W+W-1) it is the contiguous layout. For
+ * measurement only; results equal paged_decode_attn's to the same tolerance.
+ * Same arguments, workspace and errors as paged_decode_attn, plus
+ * 1 <= width <= max_blocks_per_seq * block_size (else PA_ERR_INVALID_ARG).
+ */
+pa_status paged_decode_attn_masked(uint16_t *out, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                   const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks, float scale, int32_t width,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kv_copy_blocks -- whole-block copies for copy-on-write: for every i <

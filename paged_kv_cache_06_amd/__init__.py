@@ -67,6 +67,8 @@ def lib():
     L.paged_decode_attn.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
     L.paged_decode_attn.restype = ctypes.c_int
     L.paged_decode_attn_append.argtypes = [vp] * 8 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
+    L.paged_decode_attn_masked.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, i32, vp, sz, vp]
+    L.paged_decode_attn_masked.restype = ctypes.c_int
     L.paged_decode_attn_append.restype = ctypes.c_int
     L.kv_copy_blocks.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
     L.kv_copy_blocks.restype = ctypes.c_int
@@ -174,6 +176,32 @@ def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, sca
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
     )
     _check(st, "paged_decode_attn")
+    return out
+
+
+def paged_decode_attn_masked(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, width, out=None,
+                             workspace=None, stream=None):
+    """paged_decode_attn's result computed over `width` tokens of every row,
+    positions past each row's length masked (the masked-width contrast)."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+    st = lib().paged_decode_attn_masked(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale), int(width),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
+    )
+    _check(st, "paged_decode_attn_masked")
     return out
 
 

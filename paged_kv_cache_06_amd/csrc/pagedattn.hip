@@ -377,7 +377,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int32_t* __restrict__ counters, float* __restrict__ part_ml,
-    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2) {
+    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width) {
     using K = Cfg<BS, D, NREP>;
     constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
     constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
@@ -420,7 +420,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         int carry = 0;
         for (int r0 = 0; r0 < B; r0 += 64) {
             const int r = r0 + lane;
-            const int nt = r < B ? Hkv * max(1, ((s_len[r] & kLenMask) + kTile - 1) / kTile) : 0;
+            const int Lr = r < B ? (s_len[r] & kLenMask) : 0;
+            // width > 0 (the masked-width contrast): every non-empty row spans max(width, L) tokens
+            const int nt = r < B ? Hkv * max(1, ((width > 0 && Lr > 0 ? max(width, Lr) : Lr) + kTile - 1) / kTile) : 0;
             int x = nt;
 #pragma unroll
             for (int sh = 1; sh < 64; sh <<= 1) {
@@ -451,7 +453,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
         if (!loader || !s.valid(t_end) || !s.has_tile()) return;
         const int32_t* trow = tables + (size_t)s.b * W;
         const int n0 = (s.tile * kTile) / BS;
-        const int nblk = (s.L + BS - 1) / BS;
+        const int nblk = ((width > 0 ? max(s.L, width) : s.L) + BS - 1) / BS;
         s.e0 = trow[n0];
         if constexpr (TPB > 1) {
             s.e1 = trow[n0 + 1 < nblk ? n0 + 1 : n0];
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             const int lf = __builtin_amdgcn_readfirstlane(s_len[s.b]);
             s.L = lf & kLenMask;
             s.ap = append && s.L > 0 && !(lf & kLenNoSlot);
-            s.nt = max(1, (s.L + kTile - 1) / kTile);
+            s.nt = max(1, ((width > 0 && s.L > 0 ? max(width, s.L) : s.L) + kTile - 1) / kTile);
             const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
             s.g = r / s.nt;
             s.tile = r - s.g * s.nt;
@@ -492,7 +494,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
             s.first = 1;
         }
         s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
-        s.nw = s.ap && s.tile + 1 == s.nt;
+        s.nw = s.ap && s.tile == (s.L - 1) / kTile;
         s.enew = 0;
         if (wip == 0 && s.nw) s.enew = tables[(size_t)s.b * W + (s.L - 1) / BS];
         load_entries(s);
@@ -643,10 +645,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
 #pragma unroll
             for (int h = 0; h < HPW; ++h) {
                 const float mn = fmaxf(m[h], wave_max(s[h]));
-                alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
+                const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
+                alpha[h] = __builtin_amdgcn_exp2f(m[h] - mref);
                 rescale |= alpha[h] != 1.0f;
                 m[h] = mn;
-                const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[h] - mn);
+                const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[h] - mref);
                 lsum[h] = lsum[h] * alpha[h] + (float)ph;
                 s_p[wip][h][lane] = ph;
             }
@@ -898,6 +901,7 @@ DecodeFn pick_decode(int bs, int D, int nrep) {
         case 32: return pick_d<32>(D, nrep);
         case 64: return pick_d<64>(D, nrep);
         case 128: return pick_d<128>(D, nrep);
+        case 256: return pick_d<256>(D, nrep);
         default: return {nullptr, 0};
     }
 }
@@ -1020,7 +1024,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint
                         const int32_t* block_tables, const int32_t* seq_lens, const uint16_t* k_new,
                         const uint16_t* v_new, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
-                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                        float scale, void* workspace, size_t workspace_bytes, void* stream, int32_t width = 0) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
@@ -1033,6 +1037,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint
     if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_INVALID_ARG;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_INVALID_ARG;
     if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL / 2) return PA_ERR_INVALID_ARG;
+    if (width < 0 || (long long)width > (long long)max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
     const size_t need = paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                                     max_blocks_per_seq);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -1060,7 +1065,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint
         float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
         float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
         void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
-                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2};
+                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
             hipSuccess)
             return PA_ERR_HIP;
@@ -1081,6 +1086,17 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
     return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
                          seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream);
+}
+
+pa_status paged_decode_attn_masked(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                   const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks, float scale, int32_t width,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (width <= 0) return PA_ERR_INVALID_ARG;
+    return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
+                         seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream, width);
 }
 
 pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

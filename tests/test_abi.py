@@ -31,7 +31,8 @@ def pa():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_workspace_size",
+    for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_masked",
+              "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
               "pa_status_string",
               "paged_decode_supported"]:
@@ -55,11 +56,12 @@ def test_status_strings(pa):
 
 
 def test_supported_shapes(pa):
-    for bs in (16, 32, 64, 128):
+    for bs in (16, 32, 64, 128, 256):
         for D in (64, 128):
             for nrep in (1, 2, 4, 6, 8):
                 assert pa.paged_decode_supported(2 * nrep, 2, D, bs)
     assert not pa.paged_decode_supported(12, 2, 128, 8)
+    assert not pa.paged_decode_supported(12, 2, 128, 512)
     assert not pa.paged_decode_supported(12, 2, 96, 64)
     assert not pa.paged_decode_supported(12, 5, 128, 64)
     assert not pa.paged_decode_supported(24, 2, 128, 64)  # 12 query heads per KV head
@@ -113,6 +115,21 @@ def _decode_append(L, **kw):
     return L.paged_decode_attn_append(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["t"], a["s"], a["B"],
                                       a["Hq"], a["Hkv"], a["D"], a["bs"], a["W"], a["N"],
                                       ctypes.c_float(a["scale"]), a["ws"], a["wsb"], None)
+
+
+def test_masked_width_rejects_bad_arguments_on_host(pa):
+    L = pa.lib()
+    f = FAKE
+
+    def md(width, W=4, bs=64, ws=f):
+        return L.paged_decode_attn_masked(f, f, f, f, f, f, 4, 12, 2, 128, bs, W, 16, ctypes.c_float(0.1), width,
+                                          ws, 1 << 30, None)
+
+    assert md(0) == 1
+    assert md(-5) == 1
+    assert md(4 * 64 + 1) == 1  # wider than the table
+    assert md(100, bs=24) == 2
+    assert md(100, ws=None) == 4
 
 
 def test_fused_append_rejects_bad_arguments_on_host(pa):

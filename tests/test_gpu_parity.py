@@ -211,7 +211,7 @@ def test_nan_in_dead_slots_changes_nothing(torch, pa, name):
 EDGE_LENS = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 1000, 2049]
 
 
-@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("heads", [(2, 1), (12, 2), (8, 8), (4, 1), (16, 2)])
 @pytest.mark.parametrize("D", [64, 128])
 def test_shapes_and_edge_lengths(torch, pa, oracle, bs, heads, D):
