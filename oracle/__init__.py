@@ -8,6 +8,8 @@ library and imports nothing from the product package.
 
 Pool layout the oracle reads (fp16 bit patterns as uint16):
   K: [N][Hkv][D/8][bs][8]    V: [N][Hkv][D][bs]
+FP8 pools (E4M3 codes as uint8):
+  K: [N][Hkv][D/16][bs][16]  V: [N][Hkv][D][bs]
 """
 
 from __future__ import annotations
@@ -51,6 +53,19 @@ def _load(path=None):
     lib.oracle_half_to_float.restype = None
     lib.oracle_float_to_half.argtypes = [u16p, f32p, ctypes.c_int64]
     lib.oracle_float_to_half.restype = None
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    f32 = ctypes.c_float
+    lib.oracle_fp8_to_float.argtypes = [f32p, u8p, ctypes.c_int64]
+    lib.oracle_fp8_to_float.restype = None
+    lib.oracle_float_to_fp8.argtypes = [u8p, f32p, ctypes.c_int64]
+    lib.oracle_float_to_fp8.restype = None
+    lib.oracle_quantize_fp8.argtypes = [u8p, u16p, ctypes.c_int64, f32]
+    lib.oracle_quantize_fp8.restype = None
+    lib.oracle_kv_append_fp8.argtypes = [u16p, u16p, u8p, u8p, i32p, i32p] + [i32] * 6 + [f32, f32]
+    lib.oracle_kv_append_fp8.restype = ctypes.c_int
+    lib.oracle_paged_decode_attn_fp8.argtypes = [f32p, u16p, u16p, u8p, u8p, i32p, i32p] + [i32] * 7 + [
+        f32, f32, f32, i32]
+    lib.oracle_paged_decode_attn_fp8.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_kv_copy_blocks.argtypes = [u16p, u16p, i32p, i32p] + [i32] * 5
@@ -100,6 +115,63 @@ class Oracle:
         out = np.empty(x.shape, np.uint16)
         self.lib.oracle_float_to_half(self._p(out, ctypes.c_uint16), self._p(x, ctypes.c_float), x.size)
         return out
+
+    def fp8_to_float(self, codes):
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape, np.float32)
+        self.lib.oracle_fp8_to_float(self._p(out, ctypes.c_float), self._p(codes, ctypes.c_uint8), codes.size)
+        return out
+
+    def float_to_fp8(self, x):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint8)
+        self.lib.oracle_float_to_fp8(self._p(out, ctypes.c_uint8), self._p(x, ctypes.c_float), x.size)
+        return out
+
+    def quantize_fp8(self, x, scale):
+        """fp16 array -> E4M3 codes of x / scale (uint8, same shape)."""
+        bits = self._bits(np.asarray(x, dtype=np.float16))
+        out = np.empty(bits.shape, np.uint8)
+        self.lib.oracle_quantize_fp8(self._p(out, ctypes.c_uint8), self._p(bits, ctypes.c_uint16), bits.size,
+                                     ctypes.c_float(scale))
+        return out
+
+    def kv_append_fp8(self, k_new, v_new, k_pool, v_pool, tables, seq_lens, bs, k_scale, v_scale):
+        """In-place quantizing append into uint8 pools; returns the C status."""
+        B, Hkv, D = k_new.shape
+        W = tables.shape[1]
+        N = k_pool.shape[0]
+        assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+        t = np.ascontiguousarray(tables, dtype=np.int32)
+        s = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        return self.lib.oracle_kv_append_fp8(
+            self._p(self._bits(k_new), ctypes.c_uint16), self._p(self._bits(v_new), ctypes.c_uint16),
+            self._p(k_pool, ctypes.c_uint8), self._p(v_pool, ctypes.c_uint8),
+            self._p(t, ctypes.c_int32), self._p(s, ctypes.c_int32),
+            B, Hkv, D, bs, W, N, ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+        )
+
+    def paged_decode_attn_fp8(self, q, k_pool, v_pool, tables, seq_lens, bs, scale, k_scale, v_scale, nthreads=1):
+        """FP8 pools (uint8 codes); returns (out_f32 [B][Hq][D], out_f16 [B][Hq][D])."""
+        B, Hq, D = q.shape
+        Hkv = k_pool.shape[1]
+        W = tables.shape[1]
+        N = k_pool.shape[0]
+        assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+        of = np.empty((B, Hq, D), np.float32)
+        oh = np.empty((B, Hq, D), np.uint16)
+        t = np.ascontiguousarray(tables, dtype=np.int32)
+        s = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        rc = self.lib.oracle_paged_decode_attn_fp8(
+            self._p(of, ctypes.c_float), self._p(oh, ctypes.c_uint16), self._p(self._bits(q), ctypes.c_uint16),
+            self._p(np.ascontiguousarray(k_pool), ctypes.c_uint8), self._p(np.ascontiguousarray(v_pool), ctypes.c_uint8),
+            self._p(t, ctypes.c_int32), self._p(s, ctypes.c_int32),
+            B, Hq, Hkv, D, bs, W, N,
+            ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale), int(nthreads),
+        )
+        if rc != 0:
+            raise ValueError(f"oracle_paged_decode_attn_fp8 failed: {rc}")
+        return of, oh.view(np.float16)
 
     def kv_append(self, k_new, v_new, k_pool, v_pool, tables, seq_lens, bs):
         """In-place append into k_pool / v_pool (fp16 arrays); returns the C status."""

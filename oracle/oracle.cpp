@@ -33,7 +33,9 @@
 //   K element (blk, g, t, d) at ((blk*Hkv + g)*(D/8) + d/8)*bs*8 + t*8 + d%8
 //   V element (blk, g, t, d) at ((blk*Hkv + g)*D + d)*bs + t
 // with blk a physical block id, g a KV head, t the slot in the block, d the
-// channel. fp16 values are passed as uint16_t bit patterns.
+// channel. fp16 values are passed as uint16_t bit patterns. FP8 pools (E4M3
+// bytes) use K at ((blk*Hkv + g)*(D/16) + d/16)*bs*16 + t*16 + d%16 and V at
+// the fp16 V index, one byte each.
 //
 // Pins (tests/test_oracle_pins.py): dense float64 attention and torch's
 // scaled_dot_product_attention on the numpy-gathered sequence; closed forms
@@ -41,7 +43,10 @@
 // two tokens give the logistic weight); bit-exact invariance under physical
 // block permutation, free-list history, batch position and block size;
 // kv_append against a numpy scatter; fp16 conversions against numpy over
-// every half pattern.
+// every half pattern; E4M3 decoding of all 256 codes and encoding against
+// torch's float8_e4m3fn and the format's closed-form values, the
+// quantization error bound, and the FP8 attention against the fp16 oracle
+// on pools whose dequantized values are exact in fp16.
 
 #include <cmath>
 #include <cstdint>
@@ -112,8 +117,53 @@ inline size_t v_index(int64_t blk, int g, int t, int d, int Hkv, int D, int bs) 
     return ((size_t)(blk * Hkv + g) * (size_t)D + (size_t)d) * (size_t)bs + (size_t)t;
 }
 
-// Attention for one query head over L tokens whose K/V rows are fetched by
-// the callbacks. Two-pass softmax in fp32, ascending sums.
+// 8-bit floating point, E4M3 in the OCP 8-bit floating point specification
+// (the "fn" variant: finite values and NaN only): sign bit, 4 exponent bits
+// with bias 7, 3 mantissa bits. Exponent field 0 holds zero and the
+// subnormals (m/8) * 2^-6; exponent field 15 is an ordinary binade except for
+// mantissa 7, which is NaN; there is no infinity, and the largest finite
+// magnitude is 1.75 * 2^8 = 448. Every value is exact in fp32.
+float fp8_bits_to_float(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const float mag = e == 0 ? std::ldexp((float)m, -9) : std::ldexp((float)(8 + m), e - 10);
+    return (c & 0x80) ? -mag : mag;
+}
+
+// fp32 -> E4M3: the nearest finite code by direct search over the magnitudes,
+// a tie going to the code with even mantissa; magnitudes at or above 448
+// (infinity included) saturate to 448, NaN gives code 0x7f, and the sign bit
+// is kept (a negative value that rounds to zero gives 0x80).
+uint8_t float_to_fp8_bits(float x) {
+    if (std::isnan(x)) return 0x7f;
+    const uint8_t sign = std::signbit(x) ? 0x80 : 0;
+    const double a = std::fabs((double)x);
+    if (a >= 448.0) return sign | 0x7e;
+    int best = 0;
+    for (int c = 1; c <= 0x7e; ++c) {
+        const double dc = std::fabs((double)fp8_bits_to_float((uint8_t)c) - a);
+        const double db = std::fabs((double)fp8_bits_to_float((uint8_t)best) - a);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return (uint8_t)(sign | best);
+}
+
+// The stored code of an fp16 value x in a pool quantized with scale s:
+// E4M3 of the fp32 quotient x / s (one correctly rounded fp32 division, then
+// the rounding above). Its value is code * s.
+uint8_t quantize_fp8(uint16_t x, float s) { return float_to_fp8_bits(half_bits_to_float(x) / s); }
+
+// fp8 pool layout: K element (blk, g, t, d) at
+// ((blk*Hkv + g)*(D/16) + d/16)*bs*16 + t*16 + d%16 (16 channels = 16 bytes
+// per slot and chunk); V as in the fp16 pool, one byte per element.
+inline size_t k_index8(int64_t blk, int g, int t, int d, int Hkv, int D, int bs) {
+    return ((size_t)(blk * Hkv + g) * (size_t)(D / 16) + (size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 16 +
+           (size_t)(d % 16);
+}
+
+// Attention for one query head over L tokens whose K/V elements (as fp32
+// values) are fetched by the callbacks. Two-pass softmax in fp32, ascending
+// sums.
 template <class KAt, class VAt>
 void attend_one_head(float *o, const uint16_t *qh, int L, int D, float scale, KAt k_at, VAt v_at) {
     if (L <= 0) {
@@ -123,7 +173,7 @@ void attend_one_head(float *o, const uint16_t *qh, int L, int D, float scale, KA
     std::vector<float> s((size_t)L), p((size_t)L);
     for (int t = 0; t < L; ++t) {
         float dot = 0.0f;
-        for (int d = 0; d < D; ++d) dot += half_bits_to_float(qh[d]) * half_bits_to_float(k_at(t, d));
+        for (int d = 0; d < D; ++d) dot += half_bits_to_float(qh[d]) * k_at(t, d);
         s[(size_t)t] = scale * dot;
     }
     float m = s[0];
@@ -136,13 +186,56 @@ void attend_one_head(float *o, const uint16_t *qh, int L, int D, float scale, KA
     }
     for (int d = 0; d < D; ++d) {
         float acc = 0.0f;
-        for (int t = 0; t < L; ++t) acc += p[(size_t)t] * half_bits_to_float(v_at(t, d));
+        for (int t = 0; t < L; ++t) acc += p[(size_t)t] * v_at(t, d);
         o[d] = acc / l;
     }
 }
 
 bool dims_ok(int B, int Hq, int Hkv, int D, int bs, int W) {
     return B >= 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && D > 0 && D % 8 == 0 && bs > 0 && W > 0;
+}
+
+// Driver shared by the paged attention entry points: the checks, then one
+// (row, query head) item at a time, split over `nthreads` std::threads (the
+// arithmetic of an item does not depend on the split). k_at(table, g, t, d)
+// and v_at(...) return the fp32 value of element (t, d) of KV head g of the
+// row whose block table is `table`.
+template <class KAt, class VAt>
+int paged_attend(float *out_f32, uint16_t *out_f16, const uint16_t *q, const int32_t *block_tables,
+                 const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int bs, int W, int N, float scale,
+                 int nthreads, KAt k_at, VAt v_at) {
+    const size_t cap = (size_t)W * bs;
+    for (int b = 0; b < B; ++b) {
+        const int L = seq_lens[b];
+        if (L < 0 || (size_t)L > cap) return -2;
+        for (int j = 0; j < (L + bs - 1) / bs; ++j) {
+            const int32_t blk = block_tables[(size_t)b * W + j];
+            if (blk < 0 || blk >= N) return -2;
+        }
+    }
+    const int nrep = Hq / Hkv;
+    auto work = [&](int64_t item) {
+        const int b = (int)(item / Hq), h = (int)(item % Hq), g = h / nrep;
+        const int32_t *table = block_tables + (size_t)b * W;
+        float *o = out_f32 + ((size_t)b * Hq + h) * D;
+        attend_one_head(o, q + ((size_t)b * Hq + h) * D, seq_lens[b], D, scale,
+                        [&](int t, int d) { return k_at(table, g, t, d); },
+                        [&](int t, int d) { return v_at(table, g, t, d); });
+        if (out_f16)
+            for (int d = 0; d < D; ++d) out_f16[((size_t)b * Hq + h) * D + d] = float_to_half_bits_rne(o[d]);
+    };
+    const int64_t items = (int64_t)B * Hq;
+    if (nthreads <= 1) {
+        for (int64_t i = 0; i < items; ++i) work(i);
+    } else {
+        std::vector<std::thread> pool;
+        for (int w = 0; w < nthreads; ++w)
+            pool.emplace_back([&, w] {
+                for (int64_t i = w; i < items; i += nthreads) work(i);
+            });
+        for (auto &th : pool) th.join();
+    }
+    return 0;
 }
 
 }  // namespace
@@ -157,6 +250,20 @@ void oracle_half_to_float(float *out, const uint16_t *in, int64_t n) {
 
 void oracle_float_to_half(uint16_t *out, const float *in, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = float_to_half_bits_rne(in[i]);
+}
+
+// E4M3 conversions exported so the tests can pin them against torch's
+// float8_e4m3fn and the format's closed-form values.
+void oracle_fp8_to_float(float *out, const uint8_t *in, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = fp8_bits_to_float(in[i]);
+}
+
+void oracle_float_to_fp8(uint8_t *out, const float *in, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = float_to_fp8_bits(in[i]);
+}
+
+void oracle_quantize_fp8(uint8_t *out, const uint16_t *in, int64_t n, float scale) {
+    for (int64_t i = 0; i < n; ++i) out[i] = quantize_fp8(in[i], scale);
 }
 
 // Append one decode step's K/V: row b's new token sits at position
@@ -193,6 +300,41 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_p
                 v_pool[v_index(blk, g, slot, d, Hkv, D, bs)] = v_new[((size_t)b * Hkv + g) * D + d];
             }
         }
+    }
+    return rc;
+}
+
+// The same append into an FP8 pool. A KV pool in 8-bit floats holds half the
+// bytes per token of an fp16 one; the dtype is one of the terms that set
+// bytes per token, which paging leaves alone [PagedAttention, "Three wastes
+// wearing one name" and "Checking it on a real system"]. The pages fix no
+// format or scaling; the reading taken here: E4M3 codes with one fp32 scale
+// for all of K and one for all of V, each new element stored as
+// quantize_fp8(x, scale). Same skips and return codes as oracle_kv_append.
+int oracle_kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool, uint8_t *v_pool,
+                         const int32_t *block_tables, const int32_t *seq_lens, int B, int Hkv, int D, int bs, int W,
+                         int N, float k_scale, float v_scale) {
+    if (!dims_ok(B, Hkv, Hkv, D, bs, W) || D % 16 || N <= 0) return -1;
+    int rc = 0;
+    for (int b = 0; b < B; ++b) {
+        const int L = seq_lens[b];
+        if (L < 1) continue;
+        const int pos = L - 1;
+        if (pos / bs >= W) {
+            rc = -2;
+            continue;
+        }
+        const int32_t blk = block_tables[(size_t)b * W + pos / bs];
+        if (blk < 0 || blk >= N) {
+            rc = -2;
+            continue;
+        }
+        for (int g = 0; g < Hkv; ++g)
+            for (int d = 0; d < D; ++d) {
+                const size_t i = ((size_t)b * Hkv + g) * D + d;
+                k_pool[k_index8(blk, g, pos % bs, d, Hkv, D, bs)] = quantize_fp8(k_new[i], k_scale);
+                v_pool[v_index(blk, g, pos % bs, d, Hkv, D, bs)] = quantize_fp8(v_new[i], v_scale);
+            }
     }
     return rc;
 }
@@ -304,38 +446,32 @@ int oracle_paged_decode_attn(float *out_f32, uint16_t *out_f16, const uint16_t *
                              const uint16_t *v_pool, const int32_t *block_tables, const int32_t *seq_lens, int B,
                              int Hq, int Hkv, int D, int bs, int W, int N, float scale, int nthreads) {
     if (!dims_ok(B, Hq, Hkv, D, bs, W) || N <= 0) return -1;
-    const size_t cap = (size_t)W * bs;
-    for (int b = 0; b < B; ++b) {
-        const int L = seq_lens[b];
-        if (L < 0 || (size_t)L > cap) return -2;
-        for (int j = 0; j < (L + bs - 1) / bs; ++j) {
-            const int32_t blk = block_tables[(size_t)b * W + j];
-            if (blk < 0 || blk >= N) return -2;
-        }
-    }
-    const int nrep = Hq / Hkv;
-    auto work = [&](int64_t item) {
-        const int b = (int)(item / Hq), h = (int)(item % Hq), g = h / nrep;
-        const int32_t *table = block_tables + (size_t)b * W;
-        auto k_at = [&](int t, int d) { return k_pool[k_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]; };
-        auto v_at = [&](int t, int d) { return v_pool[v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]; };
-        float *o = out_f32 + ((size_t)b * Hq + h) * D;
-        attend_one_head(o, q + ((size_t)b * Hq + h) * D, seq_lens[b], D, scale, k_at, v_at);
-        if (out_f16)
-            for (int d = 0; d < D; ++d) out_f16[((size_t)b * Hq + h) * D + d] = float_to_half_bits_rne(o[d]);
+    auto k_at = [&](const int32_t *table, int g, int t, int d) {
+        return half_bits_to_float(k_pool[k_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]);
     };
-    const int64_t items = (int64_t)B * Hq;
-    if (nthreads <= 1) {
-        for (int64_t i = 0; i < items; ++i) work(i);
-    } else {
-        std::vector<std::thread> pool;
-        for (int w = 0; w < nthreads; ++w)
-            pool.emplace_back([&, w] {
-                for (int64_t i = w; i < items; i += nthreads) work(i);
-            });
-        for (auto &th : pool) th.join();
-    }
-    return 0;
+    auto v_at = [&](const int32_t *table, int g, int t, int d) {
+        return half_bits_to_float(v_pool[v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]);
+    };
+    return paged_attend(out_f32, out_f16, q, block_tables, seq_lens, B, Hq, Hkv, D, bs, W, N, scale, nthreads, k_at,
+                        v_at);
+}
+
+// Paged decode attention over an FP8 pool: as oracle_paged_decode_attn with
+// key element value fp8(code) * k_scale and value element fp8(code) * v_scale
+// (each an fp32 product), q fp16. Same checks and return codes.
+int oracle_paged_decode_attn_fp8(float *out_f32, uint16_t *out_f16, const uint16_t *q, const uint8_t *k_pool,
+                                 const uint8_t *v_pool, const int32_t *block_tables, const int32_t *seq_lens, int B,
+                                 int Hq, int Hkv, int D, int bs, int W, int N, float scale, float k_scale,
+                                 float v_scale, int nthreads) {
+    if (!dims_ok(B, Hq, Hkv, D, bs, W) || D % 16 || N <= 0) return -1;
+    auto k_at = [&](const int32_t *table, int g, int t, int d) {
+        return fp8_bits_to_float(k_pool[k_index8(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * k_scale;
+    };
+    auto v_at = [&](const int32_t *table, int g, int t, int d) {
+        return fp8_bits_to_float(v_pool[v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * v_scale;
+    };
+    return paged_attend(out_f32, out_f16, q, block_tables, seq_lens, B, Hq, Hkv, D, bs, W, N, scale, nthreads, k_at,
+                        v_at);
 }
 
 // The same two-pass attention for one row over a contiguous sequence:
@@ -346,8 +482,8 @@ int oracle_dense_attn(float *out_f32, const uint16_t *q, const uint16_t *k, cons
     const int nrep = Hq / Hkv;
     for (int h = 0; h < Hq; ++h) {
         const int g = h / nrep;
-        auto k_at = [&](int t, int d) { return k[((size_t)t * Hkv + g) * D + d]; };
-        auto v_at = [&](int t, int d) { return v[((size_t)t * Hkv + g) * D + d]; };
+        auto k_at = [&](int t, int d) { return half_bits_to_float(k[((size_t)t * Hkv + g) * D + d]); };
+        auto v_at = [&](int t, int d) { return half_bits_to_float(v[((size_t)t * Hkv + g) * D + d]); };
         attend_one_head(out_f32 + (size_t)h * D, q + (size_t)h * D, L, D, scale, k_at, v_at);
     }
     return 0;

@@ -26,7 +26,7 @@ MUTANTS = {
     "no_normalisation": ("o[d] = acc / l;", "o[d] = acc;"),
     "denominator_not_summed": ("l += p[(size_t)t];", "l = p[(size_t)t];"),
     "group_mapping_modulo": ("h = (int)(item % Hq), g = h / nrep;", "h = (int)(item % Hq), g = h % Hkv;"),
-    "table_index_modulo": ("return k_pool[k_index(table[t / bs]", "return k_pool[k_index(table[t % bs]"),
+    "table_index_modulo": ("half_bits_to_float(k_pool[k_index(table[t / bs]", "half_bits_to_float(k_pool[k_index(table[t % bs]"),
     "k_slot_channel_swapped": ("(size_t)t * 8 +\n           (size_t)(d % 8);", "(size_t)(d % 8) * 8 +\n           (size_t)t;"),
     "v_layout_transposed": (
         "((size_t)(blk * Hkv + g) * (size_t)D + (size_t)d) * (size_t)bs + (size_t)t;",
@@ -34,7 +34,7 @@ MUTANTS = {
     ),
     "query_row_from_kv_head": ("q + ((size_t)b * Hq + h) * D, seq_lens[b]", "q + ((size_t)b * Hq + g) * D, seq_lens[b]"),
     "append_slot_off_by_one": ("const int slot = pos % bs;", "const int slot = (pos + 1) % bs;"),
-    "append_position_is_length": ("const int pos = L - 1;", "const int pos = L - 2 + (L == 1);"),
+    "append_position_is_length": ("const int pos = L - 1;\n        const int logical", "const int pos = L - 2 + (L == 1);\n        const int logical"),
     "subnormal_scale": ("5.9604644775390625e-08f", "1.1920928955078125e-07f"),
     "exponent_bias": ("((expo - 15 + 127) << 23)", "((expo - 14 + 127) << 23)"),
     "round_half_up": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;", "if (rem >= 0x1000u) h += 1;"),
@@ -49,6 +49,19 @@ MUTANTS = {
                                 "k_pool[k_index(blk, g, (t + 1) % bs, d, Hkv, D, bs)] = k_src[i];"),
     "copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)",
                              "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)"),
+    "fp8_exponent_bias": ("std::ldexp((float)(8 + m), e - 10)", "std::ldexp((float)(8 + m), e - 11)"),
+    "fp8_subnormal_scale": ("std::ldexp((float)m, -9)", "std::ldexp((float)m, -10)"),
+    "fp8_ties_away_from_zero": ("(dc == db && (c & 1) == 0)", "(dc == db)"),
+    "fp8_overflow_to_nan": ("if (a >= 448.0) return sign | 0x7e;", "if (a >= 448.0) return 0x7f;"),
+    "fp8_sign_dropped": ("return (uint8_t)(sign | best);", "return (uint8_t)best;"),
+    "fp8_quantize_multiplies": ("half_bits_to_float(x) / s", "half_bits_to_float(x) * s"),
+    "fp8_k_scale_dropped": ("k_index8(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * k_scale;",
+                            "k_index8(table[t / bs], g, t % bs, d, Hkv, D, bs)]);"),
+    "fp8_v_scaled_by_k_scale": ("v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * v_scale;",
+                                "v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * k_scale;"),
+    "fp8_k_group_of_8": ("(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 16 +", "(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 8 +"),
+    "fp8_append_slot_off_by_one": ("k_pool[k_index8(blk, g, pos % bs, d", "k_pool[k_index8(blk, g, (pos + 1) % bs, d"),
+    "fp8_append_v_with_k_scale": ("quantize_fp8(v_new[i], v_scale)", "quantize_fp8(v_new[i], k_scale)"),
 }
 
 FAST_PINS = [
@@ -67,6 +80,13 @@ FAST_PINS = [
     (pins.test_kv_append_then_attention_sees_new_token, {}),
     (pins.test_kv_copy_blocks_matches_numpy, {"shape": (2, 128, 64)}),
     (pins.test_kv_scatter_prefill_drops_the_left_padding, {}),
+    (pins.test_fp8_to_float_all_codes, {}),
+    (pins.test_float_to_fp8_matches_torch_in_range, {}),
+    (pins.test_float_to_fp8_saturates, {}),
+    (pins.test_fp8_quantization_error_bound, {}),
+    (pins.test_kv_append_fp8_matches_numpy, {}),
+    (pins.test_fp8_attention_equals_fp16_oracle_on_exact_pools, {}),
+    (pins.test_fp8_attention_matches_float64_dense, {}),
 ]
 
 

@@ -13,7 +13,14 @@
   numbers [PagedAttention, intro; "Sharing is the part that pays twice"]:
   physical block relabelling, free-list history, batch position, block size,
   and the contiguous special case;
-* kv_append against a numpy scatter of the whole pool.
+* kv_append against a numpy scatter of the whole pool;
+* FP8 (E4M3) pools: decoding of all 256 codes against torch's float8_e4m3fn
+  and the format's closed-form values, encoding against torch's cast inside
+  the finite range (ties included) and saturation outside it, the
+  quantization error bound, the quantizing append against a numpy scatter of
+  torch-quantized values, and the FP8 attention against the fp16 oracle on
+  pools whose dequantized values are exact in fp16 and against float64
+  dense attention otherwise.
 """
 
 import numpy as np
@@ -470,3 +477,142 @@ def test_validate_flags(oracle):
     twice = t.copy()
     twice[3, 1] = twice[3, 0]
     assert oracle.validate(twice, w.seq_lens, w.bs, w.N) & 16
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) pools
+# ---------------------------------------------------------------------------
+
+
+def torch_fp8_decode(codes):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def torch_fp8_encode(x):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_fp8_to_float_all_codes(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8_to_float(codes)
+    ref = torch_fp8_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))  # signed zeros included
+    # closed forms of the format: bias 7, 3 mantissa bits, subnormals below 2^-6
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x39] == 1.125 and got[0x40] == 2.0 and got[0x30] == 0.5
+    finite = got[:0x7F]
+    assert np.all(np.diff(finite) > 0)  # magnitudes increase with the code
+
+
+def test_float_to_fp8_matches_torch_in_range(oracle):
+    rng = np.random.default_rng(80)
+    mag = np.exp2(rng.uniform(-12, np.log2(447.9), size=20000)).astype(np.float32)
+    x = np.where(rng.integers(0, 2, size=mag.size) == 1, -mag, mag).astype(np.float32)
+    vals = oracle.fp8_to_float(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)  # exact ties between neighbouring codes
+    x = np.concatenate([x, mids, -mids, np.float32([0.0, -0.0, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11])])
+    assert np.all(np.abs(x) < 448)
+    got = oracle.float_to_fp8(x)
+    ref = torch_fp8_encode(x)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+    finite = np.concatenate([np.arange(0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
+    assert np.array_equal(oracle.float_to_fp8(oracle.fp8_to_float(finite)), finite)
+    # ties go to the even mantissa: 1.0625 -> 1.0 (0x38), 1.1875 -> 1.25 (0x3A)
+    assert list(oracle.float_to_fp8(np.float32([1.0625, 1.1875]))) == [0x38, 0x3A]
+
+
+def test_float_to_fp8_saturates(oracle):
+    x = np.float32([448.0, 460.0, 464.0, 500.0, 1e6, np.inf, -500.0, -np.inf, np.nan])
+    assert list(oracle.float_to_fp8(x)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F]
+
+
+def test_fp8_quantization_error_bound(oracle):
+    # code value c of x / s: |c*s - x| <= 2^-4 |x| (half a step of a 3-bit
+    # mantissa) in the normal range, <= 2^-10 s (half the subnormal step)
+    # below it, plus the fp32 rounding of the quotient
+    rng = np.random.default_rng(81)
+    for s in (1.0, 0.0371, 2.5, 2.0 ** -6):
+        x = (rng.standard_normal(50000) * rng.choice([1e-3, 0.1, 1.0, 50.0], size=50000)).astype(np.float16)
+        x = x[np.abs(x.astype(np.float64)) <= 448 * s]
+        c = oracle.quantize_fp8(x, s)
+        back = oracle.fp8_to_float(c).astype(np.float64) * s
+        xv = x.astype(np.float64)
+        err = np.abs(back - xv)
+        assert np.all(err <= 2.0 ** -4 * np.abs(xv) + 2.0 ** -10 * s + 2.0 ** -22 * np.abs(xv)), err.max()
+        assert np.array_equal(c, torch_fp8_encode(x.astype(np.float32) / np.float32(s)))
+
+
+def fp8_pool_case(seed, B=5, Hq=4, Hkv=2, D=32, bs=16, lens=(1, 15, 16, 40, 77)):
+    rng = np.random.default_rng(seed)
+    N = sum(wl.blocks_for(L, bs) for L in lens) + 4
+    w = wl.make_workload("fp8", B, Hq, Hkv, D, bs, N, list(lens), seed=seed, events=10)
+    q = wl.normal_f16(rng, (B, Hq, D))
+    kp = wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, Hkv, D, bs))
+    vp = wl.fp8_codes(rng, wl.v_pool_shape(N, Hkv, D, bs))
+    return w, q, kp, vp
+
+
+def test_kv_append_fp8_matches_numpy(oracle):
+    w, q, kp, vp = fp8_pool_case(82)
+    rng = np.random.default_rng(83)
+    kn = (wl.normal_f16(rng, (w.B, w.Hkv, w.D)).astype(np.float32) * 3).astype(np.float16)
+    vn = wl.normal_f16(rng, (w.B, w.Hkv, w.D))
+    ks, vs = 0.0371, 0.5
+    ek, ev = kp.copy(), vp.copy()
+    for b in range(w.B):
+        pos = int(w.seq_lens[b]) - 1
+        blk = int(w.tables[b, pos // w.bs])
+        for g in range(w.Hkv):
+            kc = torch_fp8_encode(kn[b, g].astype(np.float32) / np.float32(ks))
+            vc = torch_fp8_encode(vn[b, g].astype(np.float32) / np.float32(vs))
+            for d in range(w.D):
+                ek[blk, g, d // 16, pos % w.bs, d % 16] = kc[d]
+                ev[blk, g, d, pos % w.bs] = vc[d]
+    assert oracle.kv_append_fp8(kn, vn, kp, vp, w.tables, w.seq_lens, w.bs, ks, vs) == 0
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)
+
+
+def fp8_logical(oracle, w, kp, vp, ks, vs):
+    """Each row's logical [L][Hkv][D] float64 K and V from an FP8 pool (numpy reads, torch decoding)."""
+    ks_, vs_ = [], []
+    for b in range(w.B):
+        k, v = wl.read_row(kp, vp, w.tables[b], int(w.seq_lens[b]), w.bs)
+        ks_.append(torch_fp8_decode(k).astype(np.float64) * np.float32(ks))
+        vs_.append(torch_fp8_decode(v).astype(np.float64) * np.float32(vs))
+    return ks_, vs_
+
+
+def test_fp8_attention_equals_fp16_oracle_on_exact_pools(oracle):
+    # with power-of-two scales every dequantized value is exact in fp16, so
+    # the fp8 attention must equal the fp16 oracle on the converted pools bit
+    # for bit
+    w, q, kp, vp = fp8_pool_case(84)
+    ks, vs = 0.25, 2.0
+    k16 = np.empty(wl.k_pool_shape(w.N, w.Hkv, w.D, w.bs), np.float16)
+    v16 = (torch_fp8_decode(vp) * vs).astype(np.float16)
+    kl = (torch_fp8_decode(kp) * ks)  # [N][Hkv][D/16][bs][16]
+    kl = kl.transpose(0, 1, 3, 2, 4).reshape(w.N, w.Hkv, w.bs, w.D)  # [N][Hkv][bs][D]
+    k16[:] = kl.reshape(w.N, w.Hkv, w.bs, w.D // 8, 8).transpose(0, 1, 3, 2, 4).astype(np.float16)
+    assert np.array_equal(k16.astype(np.float32), kl.reshape(w.N, w.Hkv, w.bs, w.D // 8, 8).transpose(0, 1, 3, 2, 4))
+    ref, _ = oracle.paged_decode_attn(q, k16, v16, w.tables, w.seq_lens, w.bs, w.scale)
+    got, _ = oracle.paged_decode_attn_fp8(q, kp, vp, w.tables, w.seq_lens, w.bs, w.scale, ks, vs)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_fp8_attention_matches_float64_dense(oracle):
+    w, q, kp, vp = fp8_pool_case(85, lens=(3, 64, 100, 17, 250))
+    ks, vs = 0.0371, 0.113
+    got, _ = oracle.paged_decode_attn_fp8(q, kp, vp, w.tables, w.seq_lens, w.bs, w.scale, ks, vs)
+    kl, vl = fp8_logical(oracle, w, kp, vp, ks, vs)
+    for b in range(w.B):
+        ref = f64_dense(q[b], kl[b], vl[b], w.scale)
+        assert close(got[b], ref, atol=2e-6, rtol=1e-4), b
+

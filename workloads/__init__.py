@@ -14,6 +14,9 @@ Sources (page title, section):
 Pool layout (shared with every reader of the pool):
   K: [N][Hkv][D/8][bs][8]   -- 16-byte groups of 8 channels, token-minor
   V: [N][Hkv][D][bs]        -- channel-major, tokens contiguous
+FP8 pools hold one byte per element (E4M3 codes):
+  K: [N][Hkv][D/16][bs][16] -- 16-byte groups of 16 channels
+  V: [N][Hkv][D][bs]
 """
 
 from __future__ import annotations
@@ -162,6 +165,21 @@ def v_pool_shape(N, Hkv, D, bs):
     return (N, Hkv, D, bs)
 
 
+def k_pool_shape_fp8(N, Hkv, D, bs):
+    return (N, Hkv, D // 16, bs, 16)
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Random E4M3 bit patterns (uint8): a random sign bit, an exponent field
+    drawn from a rounded normal around 6.5 (magnitudes mostly 2^-3 .. 2^2)
+    and clipped to 0..14, and a uniform 3-bit mantissa. The NaN pattern
+    (exponent 15, mantissa 7) never occurs. Bits only: no conversion."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    e = np.clip(np.rint(rng.normal(6.5, 1.5, size=shape)), 0, 14).astype(np.uint8)
+    m = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | (e << 3) | m).astype(np.uint8)
+
+
 def normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
     """N(0,1) draws in float32 rounded to fp16 (round to nearest even)."""
     return rng.standard_normal(size=shape, dtype=np.float32).astype(np.float16)
@@ -193,11 +211,12 @@ def write_row(k_pool, v_pool, table_row, k_log, v_log, bs) -> None:
     """Store a row's logical K/V ([L][Hkv][D]) into the physical blocks its
     table lists (position t -> block table_row[t // bs], slot t % bs)."""
     L, Hkv, D = k_log.shape
+    grp = k_pool.shape[-1]  # channels per 16-byte group: 8 (fp16) or 16 (fp8)
     for j in range(blocks_for(L, bs)):
         blk = int(table_row[j])
         lo, hi = j * bs, min(L, (j + 1) * bs)
         n = hi - lo
-        kk = k_log[lo:hi].reshape(n, Hkv, D // 8, 8).transpose(1, 2, 0, 3)
+        kk = k_log[lo:hi].reshape(n, Hkv, D // grp, grp).transpose(1, 2, 0, 3)
         vv = v_log[lo:hi].transpose(1, 2, 0)
         k_pool[blk, :, :, :n, :] = kk
         v_pool[blk, :, :, :n] = vv
@@ -205,8 +224,8 @@ def write_row(k_pool, v_pool, table_row, k_log, v_log, bs) -> None:
 
 def read_row(k_pool, v_pool, table_row, L, bs):
     """Inverse of write_row: the row's logical [L][Hkv][D] K and V."""
-    N, Hkv, D8, _, _ = k_pool.shape
-    D = D8 * 8
+    N, Hkv, ngrp, _, grp = k_pool.shape
+    D = ngrp * grp
     k = np.empty((L, Hkv, D), k_pool.dtype)
     v = np.empty((L, Hkv, D), v_pool.dtype)
     for j in range(blocks_for(L, bs)):
