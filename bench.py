@@ -55,7 +55,8 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", "pagedattn.hip")
+# the sources of the fp16-pool decode kernel: its host side and instances, and the kernel itself
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", f) for f in ("pagedattn.hip", "decode_kernel.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_KERNEL = "decode_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -63,8 +64,11 @@ COPY_REPS = 10
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_file(workload: str) -> str:

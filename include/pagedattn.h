@@ -258,6 +258,51 @@ pa_status kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint1
                              int32_t num_blocks, int32_t padded_len, void *stream);
 
 /*
+ * FP8 pools. A pool of 8-bit floats holds half the bytes per token of an
+ * fp16 pool; the dtype is one of the terms that set bytes per token, which
+ * paging itself leaves alone [PagedAttention, "Three wastes wearing one
+ * name"; "Checking it on a real system": FP8 KV]. The pages fix neither the
+ * format nor the scaling; this library takes E4M3 as in the OCP 8-bit
+ * floating point specification (bias 7, 3 mantissa bits, no infinity, NaN
+ * = 0x7f/0xff, largest finite 448) with one fp32 scale for every K element
+ * of the pool and one for every V element: element value = code * scale.
+ *   k_pool  [N][Hkv][D/16][block_size][16] bytes (16 channels = 16 bytes,
+ *                                                token-minor)
+ *   v_pool  [N][Hkv][D][block_size]        bytes (tokens contiguous)
+ * head_dim must be a multiple of 16; block_size, head_dim and Hq/Hkv as for
+ * the fp16 pools (paged_decode_supported).
+ */
+
+/*
+ * kv_append_fp8 -- kv_append into FP8 pools: the new token's K and V
+ * elements x (fp16) are stored as the E4M3 code of x / scale, the quotient
+ * rounded to fp32 (one correctly rounded division), then to the nearest
+ * code with ties to the even mantissa; magnitudes from 448 up saturate to
+ * 448, NaN stays NaN (0x7f) and the sign is kept. Same rows skipped and same
+ * preconditions as kv_append. k_scale, v_scale: finite and > 0, else
+ * PA_ERR_INVALID_ARG; head_dim % 16 != 0 is PA_ERR_INVALID_ARG.
+ */
+pa_status kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool, uint8_t *v_pool,
+                        const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t num_blocks, float k_scale, float v_scale, void *stream);
+
+/*
+ * paged_decode_attn_fp8 -- paged_decode_attn over FP8 pools: the attention
+ * of q (fp16) over key values code * k_scale and value values code *
+ * v_scale. Codes are widened to fp16 exactly; k_scale is folded into the
+ * score scale and v_scale applied to the output. Arguments, workspace
+ * (paged_decode_workspace_size) and errors as paged_decode_attn, plus
+ * k_scale, v_scale finite and > 0 (else PA_ERR_INVALID_ARG); k_pool and
+ * v_pool 16-byte aligned.
+ */
+pa_status paged_decode_attn_fp8(uint16_t *out, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                                const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                                float v_scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

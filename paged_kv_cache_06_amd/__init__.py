@@ -1,7 +1,7 @@
 """Python binding of libpagedattn (paged KV-cache decode attention, MI355X).
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
-``libpagedattn.so`` (built from ``csrc/pagedattn.hip`` by ``build.py``).
+``libpagedattn.so`` (built from the sources under ``csrc/`` by ``build.py``).
 torch is used for device memory and streams. There is no CPU fallback: if
 the library is missing, or a tensor is not on the GPU, the call raises.
 
@@ -19,8 +19,15 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                               block_size, max_blocks_per_seq)
+  kv_append_fp8(k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                block_size, k_scale, v_scale)              (E4M3 pools)
+  paged_decode_attn_fp8(q, k_pool, v_pool, block_tables, seq_lens,
+                        block_size, scale, k_scale, v_scale, out=None,
+                        workspace=None)                    (E4M3 pools)
 
-Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16).
+Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16);
+E4M3 pools (uint8 codes, or torch.float8_e4m3fn): k_pool [N][Hkv][D/16][bs][16],
+v_pool [N][Hkv][D][bs].
 """
 
 from __future__ import annotations
@@ -74,6 +81,10 @@ def lib():
     L.kv_copy_blocks.restype = ctypes.c_int
     L.kv_scatter_prefill.argtypes = [vp] * 6 + [i32] * 7 + [vp]
     L.kv_scatter_prefill.restype = ctypes.c_int
+    L.kv_append_fp8.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_float] * 2 + [vp]
+    L.kv_append_fp8.restype = ctypes.c_int
+    L.paged_decode_attn_fp8.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float] * 3 + [vp, sz, vp]
+    L.paged_decode_attn_fp8.restype = ctypes.c_int
     L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
     L.paged_gather_kv.restype = ctypes.c_int
     _lib = L
@@ -293,3 +304,68 @@ def paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size, k_out=No
     )
     _check(st, "paged_gather_kv")
     return k_out, v_out
+
+
+def _fp8_pool(t, name):
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _dev(t, name, torch.uint8)
+    return t
+
+
+def _pool_dims_fp8(k_pool, v_pool, block_size):
+    N, Hkv, D16, bs, sixteen = k_pool.shape
+    if sixteen != 16 or bs != block_size:
+        raise ValueError(f"k_pool must be [N][Hkv][D/16][{block_size}][16], got {tuple(k_pool.shape)}")
+    D = D16 * 16
+    if tuple(v_pool.shape) != (N, Hkv, D, bs):
+        raise ValueError(f"v_pool must be {(N, Hkv, D, bs)}, got {tuple(v_pool.shape)}")
+    return N, Hkv, D
+
+
+def kv_append_fp8(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size, k_scale, v_scale,
+                  stream=None):
+    """Quantize k_new / v_new [B][Hkv][D] (fp16) to E4M3 codes of x / scale
+    and write them at position seq_lens[b]-1 of each row of the E4M3 pools."""
+    k_pool, v_pool = _fp8_pool(k_pool, "k_pool"), _fp8_pool(v_pool, "v_pool")
+    N, Hkv, D = _pool_dims_fp8(k_pool, v_pool, block_size)
+    B, W = block_tables.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be [B]")
+    st = lib().kv_append_fp8(
+        _dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hkv, D, block_size, W, N, ctypes.c_float(k_scale), ctypes.c_float(v_scale), _stream(stream),
+    )
+    _check(st, "kv_append_fp8")
+
+
+def paged_decode_attn_fp8(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, k_scale, v_scale,
+                          out=None, workspace=None, stream=None):
+    """paged_decode_attn over E4M3 pools whose elements are code * k_scale
+    (keys) and code * v_scale (values)."""
+    k_pool, v_pool = _fp8_pool(k_pool, "k_pool"), _fp8_pool(v_pool, "v_pool")
+    N, Hkv, D = _pool_dims_fp8(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+    st = lib().paged_decode_attn_fp8(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
+    )
+    _check(st, "paged_decode_attn_fp8")
+    return out
+

@@ -9,15 +9,20 @@
 //   scatter_prefill_kernel  kv_scatter_prefill: a left-padded prefill group's
 //                           K/V into the rows' blocks, padding dropped [Paged
 //                           attention, "What changed"]
+//   append_fp8_kernel       kv_append_fp8: the same append into E4M3 (FP8)
+//                           pools, quantizing [PagedAttention, "Checking it
+//                           on a real system": FP8 KV halves bytes per token]
 //   gather_kernel           paged_gather_kv: the debug path, the blocks a row
 //                           lists copied out contiguously [Paged attention,
 //                           "What changed"]
 //
-// Pool layouts (include/pagedattn.h): K [N][Hkv][D/8][bs][8], V [N][Hkv][D][bs].
+// Pool layouts (include/pagedattn.h): K [N][Hkv][D/8][bs][8], V [N][Hkv][D][bs];
+// E4M3 pools K [N][Hkv][D/16][bs][16], V [N][Hkv][D][bs], one byte each.
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 
@@ -84,6 +89,52 @@ __global__ void __launch_bounds__(64) append_kernel(const uint16_t* __restrict__
 }
 
 // One workgroup per (row, KV head, logical block); thread per (token, channel).
+// fp32 -> E4M3 code (OCP 8-bit float, bias 7, 3 mantissa bits, no
+// infinity): round to nearest, ties to even mantissa; magnitudes from 448 up
+// (infinity included) saturate to 448; NaN gives 0x7f; the sign bit is kept.
+__device__ __forceinline__ unsigned e4m3_rne_sat(float t) {
+    const unsigned u = __float_as_uint(t);
+    const unsigned sign = (u >> 24) & 0x80u;
+    const unsigned a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;          // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;  // |t| >= 448
+    if (a < 0x3c800000u) {                      // |t| < 2^-6: multiples of 2^-9 (the product is exact)
+        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8; 8 is the code of 2^-6
+        return sign | (unsigned)m;
+    }
+    // normal: round the 20 dropped mantissa bits to nearest even; a carry
+    // moves into the exponent, and |t| < 448 keeps the result at most 448
+    const unsigned r = a + 0x7ffffu + ((a >> 20) & 1u);
+    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// One wave per (row, KV head): each lane quantizes channels lane, lane+64, ...
+// of the new token's K and V (code of x / scale, the quotient correctly
+// rounded in fp32) and stores the bytes into the row's last block.
+__global__ void __launch_bounds__(64) append_fp8_kernel(const uint16_t* __restrict__ k_new,
+                                                        const uint16_t* __restrict__ v_new,
+                                                        uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                        const int32_t* __restrict__ tables,
+                                                        const int32_t* __restrict__ seq_lens, int Hkv, int D, int BS,
+                                                        int W, int N, float k_scale, float v_scale) {
+    const int bg = blockIdx.x;
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int lane = threadIdx.x;
+    const int L = seq_lens[b];
+    if (L < 1 || (long long)L > (long long)W * BS) return;
+    const int pos = L - 1;
+    const int blk = tables[(size_t)b * W + pos / BS];
+    if (blk < 0 || blk >= N) return;
+    const int slot = pos % BS;
+    const size_t base = (size_t)blk * Hkv + g;
+    const _Float16* ks = reinterpret_cast<const _Float16*>(k_new) + ((size_t)b * Hkv + g) * D;
+    const _Float16* vs = reinterpret_cast<const _Float16*>(v_new) + ((size_t)b * Hkv + g) * D;
+    for (int d = lane; d < D; d += 64) {
+        k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] = (uint8_t)e4m3_rne_sat((float)ks[d] / k_scale);
+        v_pool[(base * D + d) * BS + slot] = (uint8_t)e4m3_rne_sat((float)vs[d] / v_scale);
+    }
+}
+
 __global__ void __launch_bounds__(256) gather_kernel(uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
                                                      const uint16_t* __restrict__ k_pool,
                                                      const uint16_t* __restrict__ v_pool,
@@ -224,6 +275,24 @@ pa_status kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_po
     hipLaunchKernelGGL(append_kernel, dim3(num_seqs * num_kv_heads), dim3(64), 0, (hipStream_t)stream, k_new,
                        v_new, k_pool, v_pool, block_tables, seq_lens, num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_pool, uint8_t* v_pool,
+                        const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t num_blocks, float k_scale, float v_scale, void* stream) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+        return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
+    if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(append_fp8_kernel, dim3(num_seqs * num_kv_heads), dim3(64), 0, (hipStream_t)stream, k_new,
+                       v_new, k_pool, v_pool, block_tables, seq_lens, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, k_scale, v_scale);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -8,22 +8,10 @@
 //   [PagedAttention]      deepconcepts.dev/c/llm-paged-attention
 //   [SLM paged attention] aicassindra.com/blogs/slm/slm_paged_attention.html
 //
-// decode_kernel: one query token per row; the row's block table is walked,
-// its blocks gathered at its own length [Paged attention, "What changed";
-// PagedAttention, "What the block table costs"], and softmax attention
-// computed for the query heads of one KV group at once; long rows are split
-// over workgroups and their partial results merged exactly [PagedAttention,
-// "Sharing is the part that pays twice"]. With k_new / v_new it also performs
-// the step's kv_append [SLM paged attention, "End-to-end flow"]. It runs on
-// the vector ALU (fp16 dot2 with fp32 accumulation): decode attention is a
-// matrix-vector product per KV group, bound by HBM bandwidth, so no matrix
-// cores. The design (persistent workgroups over balanced tile ranges, a load
-// wave issuing direct-to-LDS loads, compute waves per two query heads, the
-// merge by the last partition to arrive) is described above decode_kernel.
-//
-// Stale slots and unlisted blocks may hold NaN: scores of tokens past the
-// row's length are replaced (not multiplied) by -inf, and their V halves are
-// zeroed before the dot products.
+// This file holds the host side of decode attention (argument checks, the
+// split plan, the workspace, launches) and the fp16-pool instances of
+// decode_kernel; the kernel itself is in decode_kernel.h, and the E4M3-pool
+// instances are in pagedattn_fp8.hip.
 
 #include <hip/hip_runtime.h>
 
@@ -35,820 +23,10 @@
 #include <type_traits>
 #include <utility>
 
+#include "decode_kernel.h"
 #include "pagedattn.h"
 
 namespace {
-
-constexpr int kLanes = 64;
-constexpr int kTile = 64;  // tokens per tile (one lane per token in QK)
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// wave-level helpers
-// ---------------------------------------------------------------------------
-
-// DPP controls (gfx9 encoding).
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kRowMirror = 0x140;   // lane i <-> 15-i within 16
-constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within 8
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Combine lanes i and i^16, then i and i^32, with the gfx950 permlane swaps.
-template <class Op>
-__device__ __forceinline__ float cross_rows(float x, Op op) {
-    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kQuadXor1>(x));
-    x = fmaxf(x, dpp<kQuadXor2>(x));
-    x = fmaxf(x, dpp<kHalfMirror>(x));
-    x = fmaxf(x, dpp<kRowMirror>(x));
-    return cross_rows(x, [](float a, float b) { return fmaxf(a, b); });
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp<kQuadXor1>(x);
-    x += dpp<kQuadXor2>(x);
-    x += dpp<kHalfMirror>(x);
-    x += dpp<kRowMirror>(x);
-    return cross_rows(x, [](float a, float b) { return a + b; });
-}
-
-__device__ __forceinline__ half2_t as_h2(unsigned int u) { return __builtin_bit_cast(half2_t, u); }
-
-// c + a.b over 8 fp16 pairs, fp32 accumulate (v_dot2_f32_f16).
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
-    c = __builtin_amdgcn_fdot2(as_h2(a.x), as_h2(b.x), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(b.y), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(b.z), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(b.w), c, false);
-    return c;
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Scores of one 16-byte K chunk (channel pairs 4j..4j+3) against HPW query
-// heads: a[k][h] += q_h[pair 4j+k] . k[pair k], the query pair taken from
-// lane L0+k of this lane's 16-lane row by DPP row_newbcast. The compiler
-// cannot see inside the asm, so the block carries its own wait states: two
-// before it (a VALU result read by a DPP instruction) and three after it (a
-// dot result read by a different VALU instruction). Within a block every
-// accumulator is written once, so the dots need no spacing between them.
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][1], const unsigned (&q)[1], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %4, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[1][0]), "+v"(a[2][0]), "+v"(a[3][0])
-        : "v"(q[0]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
-}
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][2], const unsigned (&q)[2], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %8, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %9, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %8, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %9, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %8, %12 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %9, %12 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %8, %13 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %9, %13 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[3][0]), "+v"(a[3][1])
-        : "v"(q[0]), "v"(q[1]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
-}
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][3], const unsigned (&q)[3], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %12, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %13, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %14, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %12, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %13, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %14, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %12, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %13, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %8, %14, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %9, %12, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %10, %13, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %11, %14, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[2][2]), "+v"(a[3][0]), "+v"(a[3][1]), "+v"(a[3][2])
-        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
-}
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][4], const unsigned (&q)[4], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %16, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %17, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %18, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %19, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %16, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %17, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %18, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %19, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %8, %16, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %9, %17, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %10, %18, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %11, %19, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %12, %16, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %13, %17, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %14, %18, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %15, %19, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[0][3]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[1][3]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[2][2]), "+v"(a[2][3]), "+v"(a[3][0]), "+v"(a[3][1]), "+v"(a[3][2]), "+v"(a[3][3])
-        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
-}
-
-// ---------------------------------------------------------------------------
-// memory helpers
-// ---------------------------------------------------------------------------
-
-// s_waitcnt immediate that waits until at most `n` vector-memory operations of
-// this wave are outstanding and does not wait on LDS/scalar or export counts
-// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int n>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// The same with a wave-uniform run-time count (a scalar branch tree over the
-// immediate forms). Counts above 63 wait for 63, which is stricter.
-template <int LO, int HI>
-__device__ __forceinline__ void wait_vmem_range(int n) {
-    if constexpr (LO == HI) {
-        wait_vmem<LO>();
-    } else {
-        constexpr int MID = (LO + HI) / 2;
-        if (n <= MID)
-            wait_vmem_range<LO, MID>(n);
-        else
-            wait_vmem_range<MID + 1, HI>(n);
-    }
-}
-__device__ __forceinline__ void wait_vmem_dyn(int n) { wait_vmem_range<0, 63>(n < 0 ? 0 : (n > 63 ? 63 : n)); }
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Workgroup barrier without a memory fence. Inside the tile loop the only
-// data shared between waves are tiles written by direct-to-LDS loads, whose
-// completion each wave establishes itself with a vmcnt wait before arriving;
-// a fenced __syncthreads would also wait for the next tiles' loads, which
-// must stay in flight. The signal fences keep the compiler from moving LDS
-// accesses across the barrier.
-__device__ __forceinline__ void tile_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Wait for this wave's LDS operations only (lgkmcnt 0; vector-memory and
-// export counts left alone), before a barrier that publishes LDS writes.
-__device__ __forceinline__ void wait_lds() {
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-    return __builtin_amdgcn_readfirstlane((unsigned)reinterpret_cast<size_t>((lds_ptr)p));
-}
-
-// The tile loop's vector-memory instructions are all issued from inline
-// assembly, so that the wave itself knows exactly how many are in flight: the
-// waits for a tile are counted from that (vm_count in the kernel), and the
-// compiler, which cannot see these instructions, inserts no waits of its own
-// for them. (Vector-memory operations of a wave complete in issue order on
-// this architecture, loads and stores alike, so "at most n outstanding"
-// means "everything issued before the last n has completed".)
-
-// One 16-byte load per lane from global memory straight into LDS: lane i's
-// bytes land at dst + 16*i (dst wave-uniform, passed in M0). One wait state
-// separates the compiler's write of M0 from the load that reads it.
-__device__ __forceinline__ void dma16(const void* src, unsigned dst) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
-}
-// Device-coherent (sc1) stores of the split-sequence partials and plain
-// stores of the output.
-__device__ __forceinline__ void st_f32_sc1(float* p, float v) {
-    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void st_2f32_sc1(float* p, float a, float b) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 v = {a, b};
-    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-// Device-coherent (sc1) loads of the partials for the merge: buffer loads
-// over one (row, KV head)'s partials, cache policy sc1 (the same coherence as
-// a relaxed agent-scope atomic load), 8 or 16 bytes per lane.
-constexpr int kCoherent = 16;                     // cache-policy bits: sc1
-constexpr int kRawBufferFormat = 0x00020000;      // dword3 of a raw 32-bit buffer resource
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
-    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
-}
-__device__ __forceinline__ void st_b128(uint16_t* p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
-}
-
-__device__ __forceinline__ int clamp_block(int blk, int N) {
-    return (unsigned)blk < (unsigned)N ? blk : 0;
-}
-
-// ---------------------------------------------------------------------------
-// decode kernel
-// ---------------------------------------------------------------------------
-
-constexpr int kMaxRows = 512;    // rows per launch (longer batches are split by the host)
-constexpr int kMaxParts = 64;    // partitions per (row, KV head)
-constexpr int kMaxPending = 4;   // split runs one workgroup may finish (at most its first and last)
-constexpr int kLenMask = 0x3fffffff;     // row length held in LDS ...
-constexpr int kLenNoSlot = 0x40000000;   // ... and a flag: the length exceeds the table, no slot to append into
-
-// Work decomposition. A row of length L has nt = ceil(L/64) tiles of 64
-// tokens per KV head (an empty row counts one tile, without data, so that its
-// zero output is written by someone). All tiles of the batch are numbered
-// row by row, KV head by KV head; workgroup w of the G' busy ones takes the
-// contiguous range [w*T/G', (w+1)*T/G') of the T tiles, so every workgroup has
-// the same work to within one tile whatever the length mix. Every workgroup
-// reads seq_lens at start and builds the prefix count of tiles per row in
-// LDS, so it finds its tiles without any host-side plan.
-//
-// A run is the part of one (row, KV head) inside one workgroup's range. A
-// (row, KV head) covered by a single workgroup is finished by it; otherwise
-// each covering workgroup stores one partial (max, sum, unnormalised output)
-// and the last to arrive merges them. G' is capped so that a workgroup gets
-// at least C tiles, which bounds the partials of a (row, KV head) by the
-// workspace's P.
-struct Pos {
-    int t;               // tile number in the batch; >= this workgroup's range end means none
-    int b, g;            // row, KV head
-    int tile;            // tile index within the row
-    int nt;              // tiles of the row (>= 1)
-    int L;               // row length (0: an empty row's only, data-less tile)
-    int k;               // ordinal of the run within this workgroup
-    int np, slot;        // workgroups covering the (row, KV head), and this one's index among them
-    int first, last;     // the run's first / last tile
-    int e0, e1, e2, e3;  // physical blocks of the tile (e1..e3 used when blocks are shorter than a tile)
-    int ap;              // the row takes this step's new token (fused append; L >= 1, within the table)
-    int nw;              // this tile holds that token (the row's last tile of an appending row)
-    int enew;            // physical block of that token (read by the wave that stores it)
-    __device__ bool valid(int t_end) const { return t < t_end; }
-    __device__ bool has_tile() const { return L > 0; }
-};
-
-// Row of tile u: the last row whose prefix count is <= u, by two rounds of a
-// 64-lane search over the LDS prefix array pre[0..B].
-__device__ __forceinline__ int find_row(const int* pre, int B, int u, int lane) {
-    const int S = (B + 63) / 64;  // rows per first-round lane
-    const int i1 = min(lane * S, B);
-    const unsigned long long m1 = __ballot(pre[i1] <= u && lane * S <= B);
-    const int r1 = (64 - __clzll(m1) - 1) * S;  // highest lane whose start is <= u
-    const int i2 = min(r1 + lane, B);
-    const unsigned long long m2 = __ballot(lane < S && pre[i2] <= u);
-    return __builtin_amdgcn_readfirstlane(r1 + (64 - __clzll(m2) - 1));
-}
-
-template <int BS, int D, int NREP>
-struct Cfg {
-    static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
-    static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
-    static constexpr int HPW = (NREP % 2 == 0) ? 2 : 1;   // query heads per compute wave
-    static constexpr int WPT = NREP / HPW;                 // compute waves, sharing every tile
-    static constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
-    static constexpr int TILE = kTile * D;                 // halves per K (or V) tile
-    static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
-    static constexpr int QI = (QC + 63) / 64;              // q load instructions
-    static constexpr int QBUF = QI * 64 * 8;               // halves per q buffer
-    static constexpr int THREADS = 64 * (WPT + 1);         // the compute waves and one load wave
-    static_assert(TPB <= 4, "block size of at least 16 tokens");
-};
-
-// decode_kernel: persistent, one workgroup per slot: WPT compute waves (one
-// per two query heads of the group, or one for a single head), which all read
-// every tile, each for its own query heads, and one load wave that issues
-// every tile load and waits for it. A wave that issues a
-// load stalls whenever the memory system is saturated; keeping all loads in
-// their own wave keeps those stalls off the compute waves.
-//
-// Tile pipeline (step j computes tile position P_j; buffers alternate by j):
-//   prologue:  load wave issues K(P0), V(P0)
-//   step j:    load wave waits for K(P_j) -> barrier A -> load wave issues
-//              [j = 0: K(P1)] V(P_{j+1}) into the V buffer freed by step j-1
-//              and waits for V(P_j) while compute waves do QK + softmax on
-//              K(P_j) -> barrier B -> load wave issues K(P_{j+2}) into the K
-//              buffer just read while compute waves do PV on V(P_j) and, if
-//              P_j ends its unit, store the unit's result
-// so 1.5 tiles of loads are in flight during every compute phase, across unit
-// boundaries as well. The query of a unit is loaded into LDS with the K tile
-// of its first position.
-//
-// Layouts: the K tile in LDS is [NJ][64 tokens][8 ch] (lane = token for QK);
-// the V tile is [NJ row blocks][8 chunks][8 rows][8 tokens], loaded so that a
-// load instruction still covers eight whole 128-byte rows of V. PV uses lane =
-// channel: lane ch reads the 8 chunks of its channel's 64 tokens, odd row
-// blocks in the order c^1, which keeps every 16-lane phase of the LDS read on
-// distinct banks. The p vector of a head (fp16, 64 tokens) is broadcast from
-// LDS. A lane thus owns whole output channels: no cross-lane reduction of the
-// output at all.
-//
-// Results: a one-partition row writes fp16 output directly; otherwise the
-// partition writes (max, sum, unnormalised output) with coherent stores and is
-// listed; at exit the workgroup adds the number of partitions it finished of
-// each (row, KV head) to that pair's arrival counter in one atomic, and merges
-// every pair whose count it completed, in partition order.
-template <int BS, int D, int NREP>
-__global__ void __launch_bounds__((Cfg<BS, D, NREP>::THREADS)) decode_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, int32_t* __restrict__ counters, float* __restrict__ part_ml,
-    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width) {
-    using K = Cfg<BS, D, NREP>;
-    constexpr int NJ = K::NJ, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
-    constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
-    static_assert(BS % 16 == 0, "block size must be a multiple of 16");
-
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[2][TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QBUF];
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t s_kn[2][D];  // fused append: the new token's K ...
-    __shared__ __attribute__((aligned(16))) uint16_t s_vn[2][D];  // ... and V, staged with the tile holding it
-    __shared__ int s_len[kMaxRows];
-    __shared__ int s_pre[kMaxRows + 1];
-    __shared__ int s_pend[kMaxPending];  // (row*Hkv + g) of split partitions finished here
-    __shared__ int s_pend_np[kMaxPending];
-    __shared__ int s_npend;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wip = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in the workgroup
-    const bool loader = wip == WPT;                             // the load wave
-    const int h0 = wip * HPW;                                   // a compute wave's first query head
-    const int Hq = Hkv * NREP;
-    const int G = gridDim.x;
-    const int cap = W * BS;
-    const int drow = lane & 7, vc = lane >> 3;  // V load lane: row within a row block, token chunk
-    const bool append = k_new != nullptr;       // fused kv_append: this step's K/V enter the pool here
-
-    // ---- tile list: lengths and the prefix count of tiles per row
-    for (int r = tid; r < B; r += THREADS) {
-        int L = seq_lens[r];
-        const int noslot = L > cap ? kLenNoSlot : 0;
-        L = L < 0 ? 0 : (L > cap ? cap : L);
-        s_len[r] = L | noslot;
-    }
-    if (tid == 0) s_npend = 0;
-    __syncthreads();
-    if (wip == 0) {
-        // serial over 64-row chunks, a wave-wide inclusive scan within each
-        int carry = 0;
-        for (int r0 = 0; r0 < B; r0 += 64) {
-            const int r = r0 + lane;
-            const int Lr = r < B ? (s_len[r] & kLenMask) : 0;
-            // width > 0 (the masked-width contrast): every non-empty row spans max(width, L) tokens
-            const int nt = r < B ? Hkv * max(1, ((width > 0 && Lr > 0 ? max(width, Lr) : Lr) + kTile - 1) / kTile) : 0;
-            int x = nt;
-#pragma unroll
-            for (int sh = 1; sh < 64; sh <<= 1) {
-                const int y = __shfl_up(x, sh);
-                if (lane >= sh) x += y;
-            }
-            if (r < B) s_pre[r + 1] = carry + x;
-            carry += __shfl(x, 63);
-        }
-        if (lane == 0) s_pre[0] = 0;
-    }
-    __syncthreads();
-    const int T = __builtin_amdgcn_readfirstlane(s_pre[B]);
-    const int Gb = min(G, max(1, T / C));  // busy workgroups: each gets at least C tiles
-    const int w = blockIdx.x;
-    const int t_begin = w < Gb ? (int)(((long long)w * T) / Gb) : 0;
-    const int t_end = w < Gb ? (int)(((long long)(w + 1) * T) / Gb) : 0;
-    auto owner = [&](int a) {  // the workgroup whose range holds tile a
-        return (int)((((long long)a + 1) * Gb + T - 1) / T) - 1;
-    };
-    wait_vmem<0>();  // nothing of the prologue is left in flight: the count below starts at zero
-    int vm_count = 0;
-
-    // table entries of a position's tile (scalar loads; entries past the
-    // row's last block are replaced by the tile's first, whose data is masked)
-    auto load_entries = [&](Pos& s) {
-        s.e0 = s.e1 = s.e2 = s.e3 = 0;
-        if (!loader || !s.valid(t_end) || !s.has_tile()) return;
-        const int32_t* trow = tables + (size_t)s.b * W;
-        const int n0 = (s.tile * kTile) / BS;
-        const int nblk = ((width > 0 ? max(s.L, width) : s.L) + BS - 1) / BS;
-        s.e0 = trow[n0];
-        if constexpr (TPB > 1) {
-            s.e1 = trow[n0 + 1 < nblk ? n0 + 1 : n0];
-            if constexpr (TPB > 2) {
-                s.e2 = trow[n0 + 2 < nblk ? n0 + 2 : n0];
-                s.e3 = trow[n0 + 3 < nblk ? n0 + 3 : n0];
-            }
-        }
-    };
-    // the position of tile t (prev: the position before it in this range)
-    auto pos_at = [&](int t, const Pos& prev, bool has_prev) {
-        Pos s;
-        if (t >= t_end) {
-            s = prev;
-            s.t = t_end;
-            return s;
-        }
-        if (has_prev && prev.tile + 1 < prev.nt) {  // the same run goes on
-            s = prev;
-            s.t = t;
-            s.tile = prev.tile + 1;
-            s.first = 0;
-        } else {
-            s.t = t;
-            s.b = find_row(s_pre, B, t, lane);
-            const int lf = __builtin_amdgcn_readfirstlane(s_len[s.b]);
-            s.L = lf & kLenMask;
-            s.ap = append && s.L > 0 && !(lf & kLenNoSlot);
-            s.nt = max(1, ((width > 0 && s.L > 0 ? max(width, s.L) : s.L) + kTile - 1) / kTile);
-            const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
-            s.g = r / s.nt;
-            s.tile = r - s.g * s.nt;
-            const int a0 = t - s.tile;  // the (row, KV head)'s first tile
-            const int w0 = owner(a0);
-            s.np = owner(a0 + s.nt - 1) - w0 + 1;
-            s.slot = w - w0;
-            s.k = has_prev ? prev.k + 1 : 0;
-            s.first = 1;
-        }
-        s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
-        s.nw = s.ap && s.tile == (s.L - 1) / kTile;
-        s.enew = 0;
-        if (wip == 0 && s.nw) s.enew = tables[(size_t)s.b * W + (s.L - 1) / BS];
-        load_entries(s);
-        return s;
-    };
-    auto entry_for = [&](const Pos& s, int idx) {  // idx = block of the tile (0..TPB-1), wave-divergent
-        if constexpr (TPB == 1) {
-            return s.e0;
-        } else if constexpr (TPB == 2) {
-            return idx == 0 ? s.e0 : s.e1;
-        } else {
-            return idx == 0 ? s.e0 : (idx == 1 ? s.e1 : (idx == 2 ? s.e2 : s.e3));
-        }
-    };
-
-    // ---- loads into LDS (issued by the load wave only); LDS byte addresses
-    const unsigned lds_k = lds_addr(&s_k[0][0]), lds_v = lds_addr(&s_v[0][0]), lds_q = lds_addr(&s_q[0][0]);
-    const unsigned lds_kn = lds_addr(&s_kn[0][0]), lds_vn = lds_addr(&s_vn[0][0]);
-    // the new token's K (or V) of a tile that holds it, staged in LDS ahead of the tile's own loads
-    auto issue_new = [&](const Pos& s, const uint16_t* src, unsigned dst) {
-        if (lane < D / 8) dma16(src + ((size_t)s.b * Hkv + s.g) * D + 8 * lane, dst);
-        vm_count += 1;
-    };
-    auto issue_q = [&](const Pos& s) {
-        const uint16_t* qrow = q + ((size_t)s.b * Hq + (size_t)s.g * NREP) * D;
-#pragma unroll
-        for (int i = 0; i < QI; ++i) {
-            const int c = i * 64 + lane;
-            dma16(qrow + 8 * min(c, QC - 1), lds_q + (unsigned)(((s.k & 1) * QBUF + i * 512) * 2));
-        }
-        vm_count += QI;
-    };
-    auto issue_k = [&](const Pos& s, int buf) {
-        if (s.nw) issue_new(s, k_new, lds_kn + (unsigned)(buf * D * 2));
-        const int tok = s.tile * kTile + lane;
-        const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : lane / BS), N);
-        const uint16_t* src = k_pool + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)(tok % BS) * 8;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) dma16(src + (size_t)j * (BS * 8), lds_k + (unsigned)((buf * TILE + j * 512) * 2));
-        vm_count += NJ;
-    };
-    auto issue_v = [&](const Pos& s, int buf) {
-        if (s.nw) issue_new(s, v_new, lds_vn + (unsigned)(buf * D * 2));
-        const int tok = s.tile * kTile + 8 * vc;
-        const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (8 * vc) / BS), N);
-        const uint16_t* src =
-            v_pool + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS);
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) dma16(src + (size_t)jj * (8 * BS), lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
-        vm_count += NJ;
-    };
-
-    // ---- per-unit state
-    constexpr int QR = NJ / 4;
-    unsigned qr[HPW][QR];
-    float m[HPW], lsum[HPW], acc[HPW][NH];
-
-    // The first tile is requested as soon as its table entries are in; the
-    // entries of the next positions are requested after it.
-    const Pos none = {};
-    Pos P0 = pos_at(t_begin, none, false);
-    int mk0 = 0, mk1 = 0, mv0 = 0, mv1 = 0;  // vm_count after each buffer's last load
-    if (loader && P0.valid(t_end) && P0.has_tile()) {
-        issue_q(P0);
-        issue_k(P0, 0);
-        mk0 = vm_count;
-        issue_v(P0, 0);
-        mv0 = vm_count;
-    }
-    Pos P1 = pos_at(t_begin + 1, P0, true);
-    Pos P2 = pos_at(t_begin + 2, P1, true);
-
-    for (int j = 0; P0.valid(t_end); ++j) {
-        const int buf = j & 1;
-        const bool tile = P0.has_tile();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
-        if (loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * kTile;
-            if (lane < D / 8)
-                *reinterpret_cast<u32x4*>(&s_k[buf][lane * 512 + tn * 8]) =
-                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
-            wait_lds();
-        }
-        tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
-        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N && lane < D / 8) {
-            // fused append: the new token's K into the pool (nothing in this launch reads it back)
-            const size_t base = (size_t)P0.enew * Hkv + P0.g;
-            st_b128(k_pool + ((base * (D / 8) + lane) * BS + (P0.L - 1) % BS) * 8,
-                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]));
-        }
-        if (loader && P1.valid(t_end) && P1.has_tile()) {
-            if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
-                if (P1.first) issue_q(P1);
-                issue_k(P1, 1);
-                mk1 = vm_count;
-            }
-            issue_v(P1, buf ^ 1);
-            if (buf) mv0 = vm_count; else mv1 = vm_count;
-        }
-        // the position after P2: its table entries are requested a whole step
-        // before anything waits on them
-        const Pos P3 = pos_at(P2.t + 1, P2, true);
-        if (!loader && tile) {
-            if (P0.first) {
-                const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.k & 1][0]) + h0 * (D / 2);
-#pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int i = 0; i < QR; ++i) qr[h][i] = qw[h * (D / 2) + 16 * i + (lane & 15)];
-#pragma unroll
-                for (int h = 0; h < HPW; ++h) {
-                    m[h] = -INFINITY;
-                    lsum[h] = 0.f;
-#pragma unroll
-                    for (int c = 0; c < NH; ++c) acc[h][c] = 0.f;
-                }
-            }
-            // ---- scores: lane = token, query pairs broadcast across lanes by DPP
-            const int t0 = P0.tile * kTile;
-            u32x4 kj[NJ];
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][jj * 512 + lane * 8]);
-            float a4[4][HPW];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int h = 0; h < HPW; ++h) a4[k][h] = 0.f;
-            [&]<int... J>(std::integer_sequence<int, J...>) {
-                ([&] {
-                    unsigned qj[HPW];
-#pragma unroll
-                    for (int h = 0; h < HPW; ++h) qj[h] = qr[h][J / 4];
-                    score_block<4 * (J % 4)>(a4, qj, kj[J]);
-                }(), ...);
-            }(std::make_integer_sequence<int, NJ>{});
-            const bool live = t0 + lane < P0.L;
-            float s[HPW];
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-                s[h] = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
-                s[h] = live ? s[h] * scale_log2 : -INFINITY;
-            }
-            // ---- online softmax (exp2 domain)
-            float alpha[HPW];
-            bool rescale = false;
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-                const float mn = fmaxf(m[h], wave_max(s[h]));
-                const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
-                alpha[h] = __builtin_amdgcn_exp2f(m[h] - mref);
-                rescale |= alpha[h] != 1.0f;
-                m[h] = mn;
-                const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[h] - mref);
-                lsum[h] = lsum[h] * alpha[h] + (float)ph;
-                s_p[wip][h][lane] = ph;
-            }
-            if (__builtin_amdgcn_readfirstlane((int)rescale)) {
-#pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int c = 0; c < NH; ++c) acc[h][c] *= alpha[h];
-            }
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
-        if (loader && tile && P0.nw) {  // fused append: the new token's V into its slot of the tile
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * kTile;
-#pragma unroll
-            for (int hv = 0; hv < NH; ++hv) {
-                const int c = hv * 64 + lane;
-                s_v[buf][(c >> 3) * 512 + (tn >> 3) * 64 + (c & 7) * 8 + (tn & 7)] = s_vn[buf][c];
-            }
-            wait_lds();
-        }
-        tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
-        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N) {
-            // fused append: the new token's V into the pool
-            const size_t base = (size_t)P0.enew * Hkv + P0.g;
-#pragma unroll
-            for (int hv = 0; hv < NH; ++hv) {
-                const int c = hv * 64 + lane;
-                st_u16(v_pool + (base * D + c) * BS + (P0.L - 1) % BS, s_vn[buf][c]);
-            }
-        }
-        if (loader && P2.valid(t_end) && P2.has_tile()) {
-            if (P2.first) issue_q(P2);
-            issue_k(P2, buf);
-            if (buf) mk1 = vm_count; else mk0 = vm_count;
-        }
-        if (!loader && tile) {
-            // ---- PV: lane = channel; chunk c of the tile read in the order c ^ par
-            const int t0 = P0.tile * kTile;
-            const int par = vc & 1;  // parity of this lane's row block (lane / 8)
-            const uint16_t* vb = &s_v[buf][(lane >> 3) * 512 + drow * 8];
-            const _Float16* pb = &s_p[wip][0][0];
-            // every LDS read of the phase first (one latency), then the dot products
-            u32x4 pv[8][HPW], vv[8][NH];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int cc = c ^ par;  // the chunk this lane reads at step c
-#pragma unroll
-                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * kTile + 8 * cc);
-#pragma unroll
-                for (int hv = 0; hv < NH; ++hv) vv[c][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8 * 512 + cc * 64);
-            }
-            if (t0 + kTile > P0.L) {  // tokens past the row's end may hold NaN: zero their V
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int n = P0.L - (t0 + 8 * (c ^ par));
-                    u32x4 mask;
-                    mask.x = (n > 0 ? 0xffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-                    mask.y = (n > 2 ? 0xffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
-                    mask.z = (n > 4 ? 0xffffu : 0u) | (n > 5 ? 0xffff0000u : 0u);
-                    mask.w = (n > 6 ? 0xffffu : 0u) | (n > 7 ? 0xffff0000u : 0u);
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) vv[c][hv] &= mask;
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-#pragma unroll
-                for (int hv = 0; hv < NH; ++hv)
-#pragma unroll
-                    for (int h = 0; h < HPW; ++h) acc[h][hv] = dot8(pv[c][h], vv[c][hv], acc[h][hv]);
-        }
-        if (!loader && P0.last) {
-            // ---- the unit's result
-            const int b = P0.b, g = P0.g;
-            float lt[HPW];
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) lt[h] = tile ? wave_sum(lsum[h]) : 1.f;
-            if (P0.np == 1) {
-                uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + h0) * D + lane;
-#pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) {
-                        const float o = tile ? acc[h][hv] / lt[h] : 0.f;
-                        st_u16(orow + h * D + hv * 64, __builtin_bit_cast(uint16_t, (_Float16)o));
-                    }
-            } else {
-                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.slot) * NREP + h0;
-                float* pa = part_acc + slot * D + lane;
-#pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) st_f32_sc1(pa + h * D + hv * 64, acc[h][hv]);
-                float* pm = part_ml + slot * 2;
-                if (lane == 0) {
-#pragma unroll
-                    for (int h = 0; h < HPW; ++h) st_2f32_sc1(pm + 2 * h, m[h], lt[h]);
-                }
-                if (wip == 0 && lane == 0) {
-                    const int n = s_npend;
-                    if (n < kMaxPending) {
-                        s_pend[n] = b * Hkv + g;
-                        s_pend_np[n] = P0.np;
-                        s_npend = n + 1;
-                    }
-                }
-            }
-        }
-        P0 = P1;
-        P1 = P2;
-        P2 = P3;
-    }
-
-    // ---- tickets and merges of split (row, KV head)s
-    __builtin_amdgcn_s_waitcnt(0);  // every partial of this workgroup is stored
-    __syncthreads();
-    const int npend = __builtin_amdgcn_readfirstlane(s_npend);
-    for (int e = tid; e < npend; e += THREADS) {
-        const int t = __hip_atomic_fetch_add(&counters[s_pend[e]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_pend_np[e] = (t + 1 == s_pend_np[e]) ? s_pend_np[e] : -s_pend_np[e];  // > 0: this workgroup merges
-    }
-    __syncthreads();
-    // Merge: every thread owns 4-channel chunks of the group's output and
-    // combines the partitions in partition order, eight at a time with all
-    // their loads in flight together (running max, rescaled sums).
-    constexpr int NC4 = NREP * D / 4;
-    constexpr int CPT = (NC4 + THREADS - 1) / THREADS;  // chunks per thread
-    constexpr int MB = CPT == 1 ? 16 : 8;               // partitions per round trip
-    for (int e = 0; e < npend; ++e) {
-        const int np = __builtin_amdgcn_readfirstlane(s_pend_np[e]);
-        if (np <= 0) continue;
-        const int bg = __builtin_amdgcn_readfirstlane(s_pend[e]);
-        const float* ml0 = part_ml + (size_t)bg * P * NREP * 2;
-        const float* acc0 = part_acc + (size_t)bg * P * NREP * D;
-        const __amdgpu_buffer_rsrc_t rml =
-            __builtin_amdgcn_make_buffer_rsrc((void*)ml0, 0, np * NREP * 2 * 4, kRawBufferFormat);
-        const __amdgpu_buffer_rsrc_t racc =
-            __builtin_amdgcn_make_buffer_rsrc((void*)acc0, 0, np * NREP * D * 4, kRawBufferFormat);
-        uint16_t* orow = out + (size_t)bg * NREP * D;  // (b*Hq + g*NREP)*D with bg = b*Hkv + g
-        float M[CPT], den[CPT];
-        f32x4 num[CPT];
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            M[i] = -INFINITY;
-            den[i] = 0.f;
-            num[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        for (int p0 = 0; p0 < np; p0 += MB) {
-            float mv[CPT][MB], lv[CPT][MB];
-            f32x4 av[CPT][MB];
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c4 = min(tid + i * THREADS, NC4 - 1);
-                const int h = (4 * c4) / D;
-#pragma unroll
-                for (int k = 0; k < MB; ++k) {
-                    const int pp = min(p0 + k, np - 1);  // past np: a repeat, weighted 0 below
-                    const f32x2 ml = __builtin_bit_cast(
-                        f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, (pp * NREP + h) * 8, 0, kCoherent));
-                    mv[i][k] = ml.x;
-                    lv[i][k] = ml.y;
-                    av[i][k] = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(racc, (pp * NREP * D + 4 * c4) * 4, 0, kCoherent));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                float mb = M[i];
-#pragma unroll
-                for (int k = 0; k < MB; ++k)
-                    if (p0 + k < np) mb = fmaxf(mb, mv[i][k]);
-                const float r = __builtin_amdgcn_exp2f(M[i] - mb);  // 0 on the first batch (M = -inf)
-                den[i] *= r;
-                num[i] *= r;
-#pragma unroll
-                for (int k = 0; k < MB; ++k) {
-                    const float w = (p0 + k < np) ? __builtin_amdgcn_exp2f(mv[i][k] - mb) : 0.f;
-                    den[i] += w * lv[i][k];
-                    num[i] += w * av[i][k];
-                }
-                M[i] = mb;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c4 = tid + i * THREADS;
-            if (c4 < NC4) {
-                const f32x4 o = num[i] / den[i];
-                typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                const f16x4 oh = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
-                *reinterpret_cast<f16x4*>(orow + 4 * c4) = oh;
-            }
-        }
-        if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-    }
-}
 
 // ---------------------------------------------------------------------------
 // workspace fill
@@ -863,48 +41,7 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
 // host side
 // ---------------------------------------------------------------------------
 
-struct DecodeFn {
-    const void* fn;
-    int threads;
-    explicit operator bool() const { return fn != nullptr; }
-};
-
-template <int BS, int D, int NREP>
-DecodeFn make_fn() {
-    return {reinterpret_cast<const void*>(decode_kernel<BS, D, NREP>), Cfg<BS, D, NREP>::THREADS};
-}
-
-template <int BS, int D>
-DecodeFn pick_nrep(int nrep) {
-    switch (nrep) {
-        case 1: return make_fn<BS, D, 1>();
-        case 2: return make_fn<BS, D, 2>();
-        case 4: return make_fn<BS, D, 4>();
-        case 6: return make_fn<BS, D, 6>();
-        case 8: return make_fn<BS, D, 8>();
-        default: return {nullptr, 0};
-    }
-}
-
-template <int BS>
-DecodeFn pick_d(int D, int nrep) {
-    switch (D) {
-        case 64: return pick_nrep<BS, 64>(nrep);
-        case 128: return pick_nrep<BS, 128>(nrep);
-        default: return {nullptr, 0};
-    }
-}
-
-DecodeFn pick_decode(int bs, int D, int nrep) {
-    switch (bs) {
-        case 16: return pick_d<16>(D, nrep);
-        case 32: return pick_d<32>(D, nrep);
-        case 64: return pick_d<64>(D, nrep);
-        case 128: return pick_d<128>(D, nrep);
-        case 256: return pick_d<256>(D, nrep);
-        default: return {nullptr, 0};
-    }
-}
+DecodeFn pick_decode(int bs, int D, int nrep) { return pick_decode_t<false>(bs, D, nrep); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -1018,18 +155,29 @@ pa_status paged_decode_workspace_init(void* workspace, size_t workspace_bytes, v
 
 namespace {
 
+// The pool's element format and its scales (E4M3 pools only; fp16 pools
+// use fp8 = false and scales of 1).
+struct PoolFormat {
+    bool fp8;
+    float k_scale, v_scale;
+};
+constexpr PoolFormat kFp16Pool = {false, 1.0f, 1.0f};
+
 // paged_decode_attn, and with k_new/v_new (non-null) the same launch with
-// kv_append of the step's K/V fused in.
-pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint16_t* v_pool,
-                        const int32_t* block_tables, const int32_t* seq_lens, const uint16_t* k_new,
-                        const uint16_t* v_new, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
-                        float scale, void* workspace, size_t workspace_bytes, void* stream, int32_t width = 0) {
+// kv_append of the step's K/V fused in (fp16 pools only).
+pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_pool, const int32_t* block_tables,
+                        const int32_t* seq_lens, const uint16_t* k_new, const uint16_t* v_new, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream, int32_t width = 0, PoolFormat fmt = kFp16Pool) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
+    if (!(std::isfinite(fmt.k_scale) && fmt.k_scale > 0.f && std::isfinite(fmt.v_scale) && fmt.v_scale > 0.f))
+        return PA_ERR_INVALID_ARG;
+    if (fmt.fp8 && (k_new || v_new)) return PA_ERR_INVALID_ARG;
     const int nrep = num_heads / num_kv_heads;
-    DecodeFn fn = pick_decode(block_size, head_dim, nrep);
+    DecodeFn fn = fmt.fp8 ? pa_detail::pick_decode_fp8(block_size, head_dim, nrep) : pick_decode(block_size, head_dim, nrep);
     if (!fn) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
@@ -1048,7 +196,8 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint
     int32_t* counters = reinterpret_cast<int32_t*>(ws + (workspace_bytes / 256 * 256 - counters_bytes(num_seqs, num_kv_heads)));
     float* part_ml = reinterpret_cast<float*>(ws);
     float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
-    float sl2 = scale * 1.4426950408889634f;
+    float sl2 = scale * fmt.k_scale * 1.4426950408889634f;
+    float vsc = fmt.v_scale;
     int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;
     // Rows are processed kMaxRows at a time (the workgroups keep the rows'
     // lengths in LDS); each launch covers its own rows of every buffer.
@@ -1065,7 +214,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, uint16_t* k_pool, uint
         float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
         float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
         void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
-                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width};
+                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &vsc};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
             hipSuccess)
             return PA_ERR_HIP;
@@ -1097,6 +246,17 @@ pa_status paged_decode_attn_masked(uint16_t* out, const uint16_t* q, const uint1
     return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
                          seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream, width);
+}
+
+pa_status paged_decode_attn_fp8(uint16_t* out, const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                                const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                                float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return launch_decode(out, q, const_cast<uint8_t*>(k_pool), const_cast<uint8_t*>(v_pool), block_tables, seq_lens,
+                         nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream, 0,
+                         PoolFormat{true, k_scale, v_scale});
 }
 
 pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

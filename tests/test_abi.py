@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_masked",
               "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
-              "pa_status_string",
+              "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8",
               "paged_decode_supported"]:
         assert n in names
 
@@ -142,6 +142,31 @@ def test_fused_append_rejects_bad_arguments_on_host(pa):
     assert _decode_append(L, bs=24) == 2
     assert _decode_append(L, wsb=100) == 4
     assert _decode_append(L, B=0) == 0  # nothing to do
+
+
+def test_fp8_calls_reject_bad_arguments_on_host(pa):
+    L = pa.lib()
+    f = FAKE
+    fl = ctypes.c_float
+
+    def dec(ks=0.5, vs=0.5, k=f, bs=64, D=128, ws=f, Hkv=2):
+        return L.paged_decode_attn_fp8(f, f, k, f, f, f, 4, 12, Hkv, D, bs, 4, 16, fl(0.1), fl(ks), fl(vs), ws,
+                                       1 << 30, None)
+
+    def app(ks=0.5, vs=0.5, D=128, k=f, B=4):
+        return L.kv_append_fp8(f, f, k, f, f, f, B, 2, D, 64, 4, 16, fl(ks), fl(vs), None)
+
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert dec(ks=bad) == 1 and dec(vs=bad) == 1
+        assert app(ks=bad) == 1 and app(vs=bad) == 1
+    assert dec(k=ctypes.c_void_p((1 << 20) + 8)) == 1  # misaligned pool
+    assert dec(Hkv=5) == 1
+    assert dec(bs=24) == 2
+    assert dec(D=96) == 2
+    assert dec(ws=None) == 4
+    assert app(D=120) == 1  # head_dim % 16
+    assert app(k=None) == 1
+    assert app(B=0) == 0  # nothing to do
 
 
 def test_copy_blocks_rejects_bad_arguments_on_host(pa):
