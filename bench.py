@@ -55,8 +55,9 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
-# the sources of the fp16-pool decode kernel: its host side and instances, and the kernel itself
-KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", f) for f in ("pagedattn.hip", "decode_kernel.h")]
+# the sources of the decode kernel: host side and fp16-pool instances, E4M3-pool instances, the kernel itself
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", f)
+               for f in ("pagedattn.hip", "pagedattn_fp8.hip", "decode_kernel.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_KERNEL = "decode_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -71,14 +72,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"decode_kernel_{workload}_traffic.txt")
+def traffic_file(workload: str, fp8: bool = False) -> str:
+    return os.path.join(PROFILES, f"decode_kernel{'_fp8' if fp8 else ''}_{workload}_traffic.txt")
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, fp8: bool = False):
     """HBM bytes per decode launch from the committed counter summary, or None
     when there is none or the kernel source changed since it was taken."""
-    path = traffic_file(workload)
+    path = traffic_file(workload, fp8)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -114,11 +115,12 @@ def _counter_per_dispatch(run_dir: str, counter: str):
     return out
 
 
-def _median_for(values: dict, needle: str, largest: int = 0):
-    """Median over the dispatches of one kernel; with `largest`, over its
-    `largest` biggest readings only (the calibration copies, not the small
-    host-device transfers the same copy kernel also serves)."""
-    got = sorted(v for name, vs in values.items() if needle in name for v in vs)
+def _median_for(values: dict, needle: str, largest: int = 0, also: str = ""):
+    """Median over the dispatches of one kernel (names holding `needle` and
+    `also`); with `largest`, over its `largest` biggest readings only (the
+    calibration copies, not the small host-device transfers the same copy
+    kernel also serves)."""
+    got = sorted(v for name, vs in values.items() if needle in name and also in name for v in vs)
     if largest:
         got = got[-largest:]
     if not got:
@@ -126,23 +128,26 @@ def _median_for(values: dict, needle: str, largest: int = 0):
     return float(np.median(got)), len(got)
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, command: str) -> str:
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, command: str,
+                fp8: bool = False) -> str:
     """Summarise two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
     into HBM bytes per decode launch, each counter scaled by its reading for a
-    plain copy of copy_bytes (which reads and writes copy_bytes once)."""
+    plain copy of copy_bytes (which reads and writes copy_bytes once). With
+    fp8, the E4M3-pool instances (the fused fp16 step's otherwise)."""
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    f_dec, n_f = _median_for(fetch, DECODE_KERNEL)
-    w_dec, n_w = _median_for(write, DECODE_KERNEL)
+    fmt = ", true>" if fp8 else ", false>"
+    f_dec, n_f = _median_for(fetch, DECODE_KERNEL, also=fmt)
+    w_dec, n_w = _median_for(write, DECODE_KERNEL, also=fmt)
     f_cpy, n_fc = _median_for(fetch, COPY_KERNEL, largest=COPY_REPS)
     w_cpy, n_wc = _median_for(write, COPY_KERNEL, largest=COPY_REPS)
     f_scale = copy_bytes / (f_cpy * 1024.0)
     w_scale = copy_bytes / (w_cpy * 1024.0)
     traffic = f_dec * 1024.0 * f_scale + w_dec * 1024.0 * w_scale
     w = wl.CONFIGS[workload]()
-    algo = decode_bytes(w, unique=True) + append_bytes(w)
+    algo = decode_bytes_fp8(w) if fp8 else decode_bytes(w, unique=True) + append_bytes(w)
     lines = [
-        f"# decode_kernel HBM traffic, workload {workload}",
+        f"# decode_kernel{' (E4M3 pools)' if fp8 else ''} HBM traffic, workload {workload}",
         f"# command: {command}",
         f"workload: {workload}",
         f"kernel_source_sha256_16: {kernel_source_hash()}",
@@ -170,6 +175,130 @@ def decode_bytes(w: wl.Workload, unique=False) -> int:
 def append_bytes(w: wl.Workload) -> int:
     rows = int(np.sum(w.seq_lens >= 1))
     return rows * w.Hkv * w.D * 2 * 2 * 2 + rows * 4 + 4 * w.B
+
+
+def decode_bytes_fp8(w: wl.Workload) -> int:
+    """As decode_bytes, with one byte per K/V element."""
+    return decode_bytes(w) - w.kv_bytes_per_layer() // 2
+
+
+def append_bytes_fp8(w: wl.Workload) -> int:
+    """The new K/V read as fp16, written as one byte per element, plus lengths and table entries."""
+    rows = int(np.sum(w.seq_lens >= 1))
+    return rows * w.Hkv * w.D * 2 * (2 + 1) + rows * 4 + 4 * w.B
+
+
+def bench_fp8(args, torch, pa):
+    """The decode step over E4M3 (FP8) pools: kv_append_fp8 then
+    paged_decode_attn_fp8 per layer, on the chosen workload's shapes with
+    random E4M3 codes in the pools; beside it the fp16 decode of the same
+    shapes (paged_decode_attn) for the ratio. Bytes count one byte per pool
+    element."""
+    w = wl.CONFIGS[args.config]()
+    layers = w.layers
+    rng = np.random.default_rng(7)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tables, lens = dev(w.tables), dev(w.seq_lens)
+    touched = decode_bytes_fp8(w) * layers
+    R = args.replicas or (1 if layers > 1 else max(1, math.ceil((1 << 30) / touched)))
+    ld = w.layer(0)
+    base = [dev(ld.q), dev(ld.k_new), dev(ld.v_new),
+            dev(wl.fp8_codes(rng, wl.k_pool_shape_fp8(w.N, w.Hkv, w.D, w.bs))),
+            dev(wl.fp8_codes(rng, wl.v_pool_shape(w.N, w.Hkv, w.D, w.bs)))]
+    sets = [[[t.clone() for t in base] for _ in range(layers)] for _ in range(R)]
+    print(f"[fp8] {w.name}: {R} replicas of {layers} layer(s) resident", file=sys.stderr, flush=True)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float16, device="cuda")
+    ws = pa.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.bs, w.W)
+    ks, vs = 0.25, 0.5
+    torch.cuda.synchronize()
+
+    def step(i):
+        for q, kn, vn, kp, vp in sets[i % R]:
+            pa.kv_append_fp8(kn, vn, kp, vp, tables, lens, w.bs, ks, vs)
+            pa.paged_decode_attn_fp8(q, kp, vp, tables, lens, w.bs, w.scale, ks, vs, out=out, workspace=ws)
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(n):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    ms_per_step = timed(step, args.steps)
+    dec_ms = timed(lambda i: pa.paged_decode_attn_fp8(sets[i % R][i % layers][0], sets[i % R][i % layers][3],
+                                                       sets[i % R][i % layers][4], tables, lens, w.bs, w.scale, ks,
+                                                       vs, out=out, workspace=ws), args.steps)
+    app_ms = timed(lambda i: pa.kv_append_fp8(sets[i % R][i % layers][1], sets[i % R][i % layers][2],
+                                               sets[i % R][i % layers][3], sets[i % R][i % layers][4], tables, lens,
+                                               w.bs, ks, vs), args.steps)
+    print(f"[fp8] step {ms_per_step * 1e3:.2f} us, decode {dec_ms * 1e3:.2f} us, append {app_ms * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+    # the fp16 decode on the same shapes (its own pools, the same number of replicas up to ~1 GiB)
+    R16 = max(1, min(R, math.ceil((1 << 30) / (decode_bytes(w) * layers))))
+    k16 = dev(ld.k_pool)
+    v16 = dev(ld.v_pool)
+    p16 = [(k16.clone(), v16.clone()) for _ in range(R16)]
+    del sets
+    f16_ms = timed(lambda i: pa.paged_decode_attn(base[0], p16[i % R16][0], p16[i % R16][1], tables, lens, w.bs,
+                                                   w.scale, out=out, workspace=ws), args.steps)
+    launch_bytes = decode_bytes_fp8(w) + append_bytes_fp8(w)
+    value = launch_bytes * layers / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = decode_bytes_fp8(w) / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged decode attention over E4M3 (FP8) KV pools: achieved HBM GB/s of the step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 q/out, e4m3 KV",
+        "data": "synthetic (random E4M3 codes, k_scale 0.25, v_scale 0.5)",
+        "config": {"workload": w.name, "batch": w.B, "layers": layers, "num_heads": w.Hq, "num_kv_heads": w.Hkv,
+                   "head_dim": w.D, "block_size": w.bs, "seq_len_sum": int(w.seq_lens.sum()), "replicas": R},
+        "rows_layers_per_s": round(w.B * layers / (ms_per_step * 1e-3), 1),
+        "bytes_per_step": launch_bytes * layers,
+        "decode_us": round(dec_ms * 1e3, 3),
+        "append_us": round(app_ms * 1e3, 3),
+        "fp16_decode_us": round(f16_ms * 1e3, 3),
+        "decode_speedup_vs_fp16": round(f16_ms / dec_ms, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(w.name, fp8=True),
+            "kernel": "decode_kernel (E4M3 pools)",
+            "bytes_per_launch": decode_bytes_fp8(w),
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+    copy_calibration(args, torch)
+
+
+def copy_calibration(args, torch):
+    """Plain device copies of a known size after the bench (the counter runs' scale)."""
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def bench_copy_blocks(args, torch, pa):
@@ -399,10 +528,12 @@ def parse():
                     help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
     ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast"],
+    ap.add_argument("--pmc-fp8", action="store_true", help="--pmc-summary of an --op fp8 run (E4M3-pool kernel)")
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast", "fp8"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
                          "scatter_prefill: the post-prefill scatter alone; contrast: the mixed batch decoded "
-                         "paged, contiguous, at masked full width, and at block sizes 16..256")
+                         "paged, contiguous, at masked full width, and at block sizes 16..256; fp8: the step "
+                         "over E4M3 pools on --config's shapes")
     ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
     return ap.parse_args()
 
@@ -411,9 +542,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         text = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.pmc_copy_mib << 20,
-                           args.pmc_command)
+                           args.pmc_command, fp8=args.pmc_fp8)
         os.makedirs(PROFILES, exist_ok=True)
-        with open(traffic_file(args.config), "w") as f:
+        with open(traffic_file(args.config, args.pmc_fp8), "w") as f:
             f.write(text)
         print(text, end="")
         return
@@ -440,6 +571,9 @@ def main():
         return
     if args.op == "contrast":
         bench_contrast(args, torch, pa)
+        return
+    if args.op == "fp8":
+        bench_fp8(args, torch, pa)
         return
     w = wl.CONFIGS[args.config]()
     layers = w.layers
@@ -618,14 +752,7 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
-
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(COPY_REPS):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_calibration(args, torch)
 
 
 if __name__ == "__main__":

@@ -57,7 +57,11 @@ namespace {
 using pa_detail::DecodeFn;
 
 constexpr int kLanes = 64;
-constexpr int kTile = 64;  // tokens per tile (one lane per token in QK)
+// Tokens per tile: 64 for fp16 pools, 128 for E4M3 pools, so that a tile is
+// 16 KiB of K and 16 KiB of V at head_dim 128 in either format (the bytes a
+// workgroup keeps in flight set its share of the bandwidth). One lane per
+// token of each 64-token half in QK.
+constexpr int tile_tokens(bool f8) { return f8 ? 128 : 64; }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -127,6 +131,14 @@ template <int H>
 __device__ __forceinline__ u32x4 widen8(const u32x4& r) {
     const unsigned a = H ? r.z : r.x, b = H ? r.w : r.y;
     return u32x4{f8x2<false>(a), f8x2<true>(a), f8x2<false>(b), f8x2<true>(b)};
+}
+// Mask that keeps the first n (0..16 after clamping) bytes of a 16-byte chunk.
+__device__ __forceinline__ u32x4 keep_first_bytes(int n) {
+    auto word = [n](int w) {
+        const int k = n - 4 * w;  // bytes of this word to keep
+        return k >= 4 ? 0xffffffffu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
+    };
+    return u32x4{word(0), word(1), word(2), word(3)};
 }
 // Mask that keeps the first n (0..8 after clamping) fp16 values of a chunk of 8.
 __device__ __forceinline__ u32x4 keep_first(int n) {
@@ -344,7 +356,8 @@ struct Pos {
     int k;               // ordinal of the run within this workgroup
     int np, slot;        // workgroups covering the (row, KV head), and this one's index among them
     int first, last;     // the run's first / last tile
-    int e0, e1, e2, e3;  // physical blocks of the tile (e1..e3 used when blocks are shorter than a tile)
+    int e0, e1, e2, e3;  // physical blocks of the tile (e1.. used when blocks are shorter than a tile)
+    int e4, e5, e6, e7;
     int ap;              // the row takes this step's new token (fused append; L >= 1, within the table)
     int nw;              // this tile holds that token (the row's last tile of an appending row)
     int enew;            // physical block of that token (read by the wave that stores it)
@@ -368,18 +381,21 @@ template <int BS, int D, int NREP, bool F8>
 struct Cfg {
     static constexpr int E = F8 ? 1 : 2;                   // bytes per pool element (E4M3 or fp16)
     static constexpr int G16 = 16 / E;                     // K channels per 16-byte group; V tokens per 16 bytes
-    static constexpr int NJ = D / G16;                     // 1 KiB load instructions per K (and per V) tile
+    static constexpr int TT = tile_tokens(F8);             // tokens per tile
+    static constexpr int HALVES = TT / 64;                 // 64-token halves of a tile
+    static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
+    static constexpr int NJH = NJ / HALVES;                // K load instructions per half (one per channel group)
     static constexpr int NC = D / 8;                       // 8-channel fp16 chunks of a K row in the scores
     static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
     static constexpr int HPW = (NREP % 2 == 0) ? 2 : 1;   // query heads per compute wave
     static constexpr int WPT = NREP / HPW;                 // compute waves, sharing every tile
-    static constexpr int TPB = BS >= kTile ? 1 : kTile / BS;  // blocks per tile
-    static constexpr int TILE = kTile * D * E / 2;         // LDS halves per K (or V) tile
+    static constexpr int TPB = BS >= TT ? 1 : TT / BS;     // blocks per tile
+    static constexpr int TILE = TT * D * E / 2;            // LDS halves per K (or V) tile
     static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
     static constexpr int QI = (QC + 63) / 64;              // q load instructions
     static constexpr int QBUF = QI * 64 * 8;               // halves per q buffer
     static constexpr int THREADS = 64 * (WPT + 1);         // the compute waves and one load wave
-    static_assert(TPB <= 4, "block size of at least 16 tokens");
+    static_assert(TPB <= 8, "block size of at least 16 tokens");
 };
 
 // decode_kernel: persistent, one workgroup per slot: WPT compute waves (one
@@ -423,14 +439,14 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float v_scale) {
     using K = Cfg<BS, D, NREP, F8>;
     constexpr int NJ = K::NJ, NC = K::NC, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
-    constexpr int E = K::E, G16 = K::G16;
+    constexpr int E = K::E, G16 = K::G16, TT = K::TT, HALVES = K::HALVES, NJH = K::NJH;
     constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
     static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_v[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QBUF];
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][kTile];
+    __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][TT];
     __shared__ __attribute__((aligned(16))) uint16_t s_kn[2][D];  // fused append: the new token's K ...
     __shared__ __attribute__((aligned(16))) uint16_t s_vn[2][D];  // ... and V, staged with the tile holding it
     __shared__ int s_len[kMaxRows];
@@ -447,8 +463,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     const int Hq = Hkv * NREP;
     const int G = gridDim.x;
     const int cap = W * BS;
-    // V load lane: row (channel) within the instruction's rows, and chunk of G16 tokens
-    const int drow = lane % G16, vc = lane / G16;
+    // V load lane: row (channel) among the instruction's 8, and chunk of G16 tokens (8 chunks per tile)
+    const int drow = lane & 7, vc = lane >> 3;
     const bool append = !F8 && k_new != nullptr;  // fused kv_append (fp16 pools): this step's K/V enter the pool here
 
     // ---- tile list: lengths and the prefix count of tiles per row
@@ -467,7 +483,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             const int r = r0 + lane;
             const int Lr = r < B ? (s_len[r] & kLenMask) : 0;
             // width > 0 (the masked-width contrast): every non-empty row spans max(width, L) tokens
-            const int nt = r < B ? Hkv * max(1, ((width > 0 && Lr > 0 ? max(width, Lr) : Lr) + kTile - 1) / kTile) : 0;
+            const int nt = r < B ? Hkv * max(1, ((width > 0 && Lr > 0 ? max(width, Lr) : Lr) + TT - 1) / TT) : 0;
             int x = nt;
 #pragma unroll
             for (int sh = 1; sh < 64; sh <<= 1) {
@@ -494,18 +510,23 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     // table entries of a position's tile (scalar loads; entries past the
     // row's last block are replaced by the tile's first, whose data is masked)
     auto load_entries = [&](Pos& s) {
-        s.e0 = s.e1 = s.e2 = s.e3 = 0;
+        s.e0 = s.e1 = s.e2 = s.e3 = s.e4 = s.e5 = s.e6 = s.e7 = 0;
         if (!loader || !s.valid(t_end) || !s.has_tile()) return;
         const int32_t* trow = tables + (size_t)s.b * W;
-        const int n0 = (s.tile * kTile) / BS;
+        const int n0 = (s.tile * TT) / BS;
         const int nblk = ((width > 0 ? max(s.L, width) : s.L) + BS - 1) / BS;
+        auto at = [&](int i) { return trow[n0 + i < nblk ? n0 + i : n0]; };
         s.e0 = trow[n0];
-        if constexpr (TPB > 1) {
-            s.e1 = trow[n0 + 1 < nblk ? n0 + 1 : n0];
-            if constexpr (TPB > 2) {
-                s.e2 = trow[n0 + 2 < nblk ? n0 + 2 : n0];
-                s.e3 = trow[n0 + 3 < nblk ? n0 + 3 : n0];
-            }
+        if constexpr (TPB > 1) s.e1 = at(1);
+        if constexpr (TPB > 2) {
+            s.e2 = at(2);
+            s.e3 = at(3);
+        }
+        if constexpr (TPB > 4) {
+            s.e4 = at(4);
+            s.e5 = at(5);
+            s.e6 = at(6);
+            s.e7 = at(7);
         }
     };
     // the position of tile t (prev: the position before it in this range)
@@ -527,7 +548,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             const int lf = __builtin_amdgcn_readfirstlane(s_len[s.b]);
             s.L = lf & kLenMask;
             s.ap = append && s.L > 0 && !(lf & kLenNoSlot);
-            s.nt = max(1, ((width > 0 && s.L > 0 ? max(width, s.L) : s.L) + kTile - 1) / kTile);
+            s.nt = max(1, ((width > 0 && s.L > 0 ? max(width, s.L) : s.L) + TT - 1) / TT);
             const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
             s.g = r / s.nt;
             s.tile = r - s.g * s.nt;
@@ -539,7 +560,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             s.first = 1;
         }
         s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
-        s.nw = s.ap && s.tile == (s.L - 1) / kTile;
+        s.nw = s.ap && s.tile == (s.L - 1) / TT;
         s.enew = 0;
         if (wip == 0 && s.nw) s.enew = tables[(size_t)s.b * W + (s.L - 1) / BS];
         load_entries(s);
@@ -550,8 +571,12 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             return s.e0;
         } else if constexpr (TPB == 2) {
             return idx == 0 ? s.e0 : s.e1;
-        } else {
+        } else if constexpr (TPB == 4) {
             return idx == 0 ? s.e0 : (idx == 1 ? s.e1 : (idx == 2 ? s.e2 : s.e3));
+        } else {
+            const int lo = idx == 0 ? s.e0 : (idx == 1 ? s.e1 : (idx == 2 ? s.e2 : s.e3));
+            const int hi = idx == 4 ? s.e4 : (idx == 5 ? s.e5 : (idx == 6 ? s.e6 : s.e7));
+            return idx < 4 ? lo : hi;
         }
     };
 
@@ -574,23 +599,27 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     };
     auto issue_k = [&](const Pos& s, int buf) {
         if (s.nw) issue_new(s, k_new, lds_kn + (unsigned)(buf * D * 2));
-        const int tok = s.tile * kTile + lane;
-        const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : lane / BS), N);
-        const char* src = reinterpret_cast<const char*>(k_pool) + ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) * E +
-                          (size_t)(tok % BS) * 16;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) dma16(src + (size_t)j * (BS * 16), lds_k + (unsigned)((buf * TILE + j * 512) * 2));
+        for (int hf = 0; hf < HALVES; ++hf) {  // lane = token of the half; one instruction per channel group
+            const int tok = s.tile * TT + 64 * hf + lane;
+            const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (64 * hf + lane) / BS), N);
+            const char* src = reinterpret_cast<const char*>(k_pool) +
+                              ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) * E + (size_t)(tok % BS) * 16;
+#pragma unroll
+            for (int j = 0; j < NJH; ++j)
+                dma16(src + (size_t)j * (BS * 16), lds_k + (unsigned)((buf * TILE + (hf * NJH + j) * 512) * 2));
+        }
         vm_count += NJ;
     };
     auto issue_v = [&](const Pos& s, int buf) {
         if (s.nw) issue_new(s, v_new, lds_vn + (unsigned)(buf * D * 2));
-        const int tok = s.tile * kTile + G16 * vc;
+        const int tok = s.tile * TT + G16 * vc;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (G16 * vc) / BS), N);
         const char* src = reinterpret_cast<const char*>(v_pool) +
                           (((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS)) * E;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-            dma16(src + (size_t)jj * (G16 * BS) * E, lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
+        for (int jj = 0; jj < NJ; ++jj)  // rows 8jj .. 8jj+7
+            dma16(src + (size_t)jj * (8 * BS) * E, lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
         vm_count += NJ;
     };
 
@@ -621,7 +650,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
         if (!F8 && loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * kTile;
+            const int tn = P0.L - 1 - P0.tile * TT;
             if (lane < D / 8)
                 *reinterpret_cast<u32x4*>(&s_k[buf][lane * 512 + tn * 8]) =
                     *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
@@ -661,48 +690,62 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     for (int c = 0; c < NH; ++c) acc[h][c] = 0.f;
                 }
             }
-            // ---- scores: lane = token, query pairs broadcast across lanes by DPP
-            // (an E4M3 tile: each 16-channel chunk widened to two fp16 chunks as it is used)
-            const int t0 = P0.tile * kTile;
-            u32x4 kj[NJ];
+            // ---- scores: lane = token of each 64-token half, query pairs
+            // broadcast across lanes by DPP (an E4M3 tile: each 16-channel
+            // chunk is widened to two fp16 chunks as it is used)
+            const int t0 = P0.tile * TT;
+            float s[HALVES][HPW];
 #pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][jj * 512 + lane * 8]);
-            float a4[4][HPW];
+            for (int hf = 0; hf < HALVES; ++hf) {
+                u32x4 kj[NJH];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+                for (int jj = 0; jj < NJH; ++jj)
+                    kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][(hf * NJH + jj) * 512 + lane * 8]);
+                float a4[4][HPW];
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) a4[k][h] = 0.f;
-            [&]<int... J>(std::integer_sequence<int, J...>) {
-                ([&] {
-                    unsigned qj[HPW];
+                for (int k = 0; k < 4; ++k)
 #pragma unroll
-                    for (int h = 0; h < HPW; ++h) qj[h] = qr[h][J / 4];
-                    if constexpr (F8)
-                        score_block<4 * (J % 4)>(a4, qj, widen8<J % 2>(kj[J / 2]));
-                    else
-                        score_block<4 * (J % 4)>(a4, qj, kj[J]);
-                }(), ...);
-            }(std::make_integer_sequence<int, NC>{});
-            const bool live = t0 + lane < P0.L;
-            float s[HPW];
+                    for (int h = 0; h < HPW; ++h) a4[k][h] = 0.f;
+                [&]<int... J>(std::integer_sequence<int, J...>) {
+                    ([&] {
+                        unsigned qj[HPW];
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-                s[h] = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
-                s[h] = live ? s[h] * scale_log2 : -INFINITY;
+                        for (int h = 0; h < HPW; ++h) qj[h] = qr[h][J / 4];
+                        if constexpr (F8)
+                            score_block<4 * (J % 4)>(a4, qj, widen8<J % 2>(kj[J / 2]));
+                        else
+                            score_block<4 * (J % 4)>(a4, qj, kj[J]);
+                    }(), ...);
+                }(std::make_integer_sequence<int, NC>{});
+                const bool live = t0 + 64 * hf + lane < P0.L;
+#pragma unroll
+                for (int h = 0; h < HPW; ++h) {
+                    const float d = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
+                    s[hf][h] = live ? d * scale_log2 : -INFINITY;
+                }
+                if constexpr (HALVES > 1) __builtin_amdgcn_sched_barrier(0);  // one half's K chunks live at a time
             }
             // ---- online softmax (exp2 domain)
             float alpha[HPW];
             bool rescale = false;
 #pragma unroll
             for (int h = 0; h < HPW; ++h) {
-                const float mn = fmaxf(m[h], wave_max(s[h]));
+                float smax = s[0][h];
+#pragma unroll
+                for (int hf = 1; hf < HALVES; ++hf) smax = fmaxf(smax, s[hf][h]);
+                const float mn = fmaxf(m[h], wave_max(smax));
                 const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
                 alpha[h] = __builtin_amdgcn_exp2f(m[h] - mref);
                 rescale |= alpha[h] != 1.0f;
                 m[h] = mn;
-                const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[h] - mref);
-                lsum[h] = lsum[h] * alpha[h] + (float)ph;
-                s_p[wip][h][lane] = ph;
+                float ps = 0.f;
+#pragma unroll
+                for (int hf = 0; hf < HALVES; ++hf) {
+                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[hf][h] - mref);
+                    ps += (float)ph;
+                    s_p[wip][h][64 * hf + lane] = ph;
+                }
+                lsum[h] = lsum[h] * alpha[h] + ps;
             }
             if (__builtin_amdgcn_readfirstlane((int)rescale)) {
 #pragma unroll
@@ -715,12 +758,23 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
         if (!F8 && loader && tile && P0.nw) {  // fused append: the new token's V into its slot of the tile
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * kTile;
+            const int tn = P0.L - 1 - P0.tile * TT;
 #pragma unroll
             for (int hv = 0; hv < NH; ++hv) {
                 const int c = hv * 64 + lane;
                 s_v[buf][(c >> 3) * 512 + (tn >> 3) * 64 + (c & 7) * 8 + (tn & 7)] = s_vn[buf][c];
             }
+            wait_lds();
+        }
+        if (F8 && loader && tile && P0.tile * TT + TT > P0.L) {
+            // an E4M3 tile past the row's end: its dead slots may hold NaN
+            // codes; they are zeroed in LDS here (lane = chunk*8 + row, one
+            // 16-byte unit per instruction), so PV needs no masking
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const u32x4 mask = keep_first_bytes(P0.L - (P0.tile * TT + 16 * vc));
+            char* vt = reinterpret_cast<char*>(&s_v[buf][0]) + 16 * lane;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<u32x4*>(vt + jj * 1024) &= mask;
             wait_lds();
         }
         tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
@@ -740,7 +794,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         }
         if (!F8 && !loader && tile) {
             // ---- PV: lane = channel; chunk c of the tile read in the order c ^ par
-            const int t0 = P0.tile * kTile;
+            const int t0 = P0.tile * TT;
             const int par = vc & 1;  // parity of this lane's row block (lane / 8)
             const uint16_t* vb = &s_v[buf][(lane >> 3) * 512 + drow * 8];
             const _Float16* pb = &s_p[wip][0][0];
@@ -750,11 +804,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             for (int c = 0; c < 8; ++c) {
                 const int cc = c ^ par;  // the chunk this lane reads at step c
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * kTile + 8 * cc);
+                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * TT + 8 * cc);
 #pragma unroll
                 for (int hv = 0; hv < NH; ++hv) vv[c][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8 * 512 + cc * 64);
             }
-            if (t0 + kTile > P0.L) {  // tokens past the row's end may hold NaN: zero their V
+            if (t0 + TT > P0.L) {  // tokens past the row's end may hold NaN: zero their V
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const u32x4 mask = keep_first(P0.L - (t0 + 8 * (c ^ par)));
@@ -770,36 +824,46 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     for (int h = 0; h < HPW; ++h) acc[h][hv] = dot8(pv[c][h], vv[c][hv], acc[h][hv]);
         }
         if (F8 && !loader && tile) {
-            // ---- PV over an E4M3 tile: lane = channel c, whose 64 tokens are
-            // four 16-byte chunks at (c/16)*1 KiB + chunk*256 + (c%16)*16
-            const int t0 = P0.tile * kTile;
-            const char* vb = reinterpret_cast<const char*>(&s_v[buf][0]) + (lane >> 4) * 1024 + (lane & 15) * 16;
+            // ---- PV over an E4M3 tile of 128 tokens: lane = channel. The tile's
+            // bytes sit as the fp16 tile's do: instruction c/8, then 8 chunks
+            // of 16 tokens, each 8 rows of 16 bytes; chunk k read at step
+            // k ^ par, as above. Codes past the row's end were zeroed in LDS
+            // by the load wave.
+            const int par = vc & 1;
+            const char* vb = reinterpret_cast<const char*>(&s_v[buf][0]) + (lane >> 3) * 1024 + drow * 16;
             const _Float16* pb = &s_p[wip][0][0];
-            u32x4 pv[8][HPW], vr[4][NH];
+            // two groups of four chunks, each group's LDS reads issued together;
+            // the scheduling barrier keeps the second group's reads (and
+            // registers) out of the first group's arithmetic
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
+            for (int grp = 0; grp < 2; ++grp) {
+                u32x4 vr[4][NH], pv[4][2][HPW];
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * kTile + 8 * c);
+                for (int k = 0; k < 4; ++k) {
+                    const int kk = (4 * grp + k) ^ par;  // tokens 16kk .. 16kk+15
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+                    for (int hv = 0; hv < NH; ++hv)
+                        vr[k][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8192 + kk * 128);
 #pragma unroll
-                for (int hv = 0; hv < NH; ++hv) vr[k][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 4096 + k * 256);
-            const bool tail = t0 + kTile > P0.L;  // tokens past the row's end may hold NaN: zero their V
+                    for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+                        for (int h = 0; h < HPW; ++h)
+                            pv[k][c][h] = *reinterpret_cast<const u32x4*>(pb + h * TT + 16 * kk + 8 * c);
+                }
 #pragma unroll
-                for (int hv = 0; hv < NH; ++hv) {
-                    u32x4 lo = widen8<0>(vr[k][hv]), hi = widen8<1>(vr[k][hv]);
-                    if (tail) {
-                        lo &= keep_first(P0.L - (t0 + 16 * k));
-                        hi &= keep_first(P0.L - (t0 + 16 * k + 8));
-                    }
+                for (int k = 0; k < 4; ++k) {
 #pragma unroll
-                    for (int h = 0; h < HPW; ++h) {
-                        acc[h][hv] = dot8(pv[2 * k][h], lo, acc[h][hv]);
-                        acc[h][hv] = dot8(pv[2 * k + 1][h], hi, acc[h][hv]);
+                    for (int hv = 0; hv < NH; ++hv) {
+                        const u32x4 lo = widen8<0>(vr[k][hv]), hi = widen8<1>(vr[k][hv]);
+#pragma unroll
+                        for (int h = 0; h < HPW; ++h) {
+                            acc[h][hv] = dot8(pv[k][0][h], lo, acc[h][hv]);
+                            acc[h][hv] = dot8(pv[k][1][h], hi, acc[h][hv]);
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (!loader && P0.last) {
             // ---- the unit's result

@@ -47,7 +47,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Split bounds, fixed on the host from sizes alone (no device value is read):
 // at most P = min(kMaxParts, tiles of a full row) partials per (row, KV head),
-// which holds when every busy workgroup takes at least C tiles.
+// which holds when every busy workgroup takes at least C tiles. Tiles are
+// tt tokens (tile_tokens of the pool format); the workspace is sized with
+// the fp16 pools' 64-token tiles, which give the larger P.
 struct Plan {
     long long wtiles;  // tiles of a full-width row
     int rows;          // rows per launch
@@ -55,9 +57,9 @@ struct Plan {
     int P;             // partials per (row, KV head), at most
 };
 
-Plan make_plan(int B, int Hkv, int bs, int W) {
+Plan make_plan(int B, int Hkv, int bs, int W, int tt) {
     Plan pl;
-    pl.wtiles = ((long long)W * bs + kTile - 1) / kTile;
+    pl.wtiles = ((long long)W * bs + tt - 1) / tt;
     pl.rows = std::max(1, std::min(B, kMaxRows));
     pl.P = (int)std::min<long long>(kMaxParts, pl.wtiles);
     // a (row, KV head) of nt tiles meets at most 1 + ceil((nt-1)/C) ranges of >= C tiles
@@ -138,7 +140,7 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
         block_size <= 0 || max_blocks_per_seq <= 0)
         return 0;
     const size_t rows = (size_t)(num_seqs > 0 ? num_seqs : 1);
-    const Plan pl = make_plan((int)rows, num_kv_heads, block_size, max_blocks_per_seq);
+    const Plan pl = make_plan((int)rows, num_kv_heads, block_size, max_blocks_per_seq, tile_tokens(false));
     return partials_bytes((int)rows, num_heads, head_dim, pl.P) + counters_bytes((int)rows, num_kv_heads);
 }
 
@@ -190,7 +192,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
                                                     max_blocks_per_seq);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return PA_ERR_WORKSPACE;
-    const Plan pl = make_plan(num_seqs, num_kv_heads, block_size, max_blocks_per_seq);
+    const Plan pl = make_plan(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, tile_tokens(fmt.fp8));
     const int slots = blocks_per_cu(fn) * cu_count();
     char* ws = static_cast<char*>(workspace);
     int32_t* counters = reinterpret_cast<int32_t*>(ws + (workspace_bytes / 256 * 256 - counters_bytes(num_seqs, num_kv_heads)));
