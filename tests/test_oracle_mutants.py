@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -120,16 +121,32 @@ def _run_pins(lib_path):
     return failed
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(name, tmp_path):
-    old, new = MUTANTS[name]
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Every mutant built and run against the fast pins once, in parallel
+    (each in its own child process): {name: failing pin names, or exception}."""
     src = open(oracle_pkg.SRC).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
-    mutant_src = tmp_path / "oracle_mutant.cpp"
-    mutant_src.write_text(src.replace(old, new))
-    lib = str(tmp_path / "liboracle_mutant.so")
-    subprocess.run(["g++", *oracle_pkg.CXXFLAGS, str(mutant_src), "-o", lib], check=True)
-    failed = _failing_pins(lib)
+    root = tmp_path_factory.mktemp("mutants")
+
+    def build(name):
+        old, new = MUTANTS[name]
+        if src.count(old) != 1:
+            return AssertionError(f"mutation anchor for {name} not unique")
+        path = root / f"{name}.cpp"
+        path.write_text(src.replace(old, new))
+        lib = str(root / f"lib{name}.so")
+        subprocess.run(["g++", *oracle_pkg.CXXFLAGS, str(path), "-o", lib], check=True)
+        return _failing_pins(lib)
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        return dict(zip(sorted(MUTANTS), ex.map(build, sorted(MUTANTS))))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, mutant_results):
+    failed = mutant_results[name]
+    if isinstance(failed, Exception):
+        raise failed
     assert failed, f"no pin caught mutant {name}"
 
 
