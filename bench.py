@@ -57,7 +57,7 @@ PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 # the sources of the decode kernel: host side and fp16-pool instances, E4M3-pool instances, the kernel itself
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", f)
-               for f in ("pagedattn.hip", "pagedattn_fp8.hip", "decode_kernel.h")]
+               for f in ("pagedattn.hip", "pagedattn_fp8.hip", "decode_kernel.h", "e4m3.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_KERNEL = "decode_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -189,8 +189,9 @@ def append_bytes_fp8(w: wl.Workload) -> int:
 
 
 def bench_fp8(args, torch, pa):
-    """The decode step over E4M3 (FP8) pools: kv_append_fp8 then
-    paged_decode_attn_fp8 per layer, on the chosen workload's shapes with
+    """The decode step over E4M3 (FP8) pools: one fused launch per layer
+    (paged_decode_attn_append_fp8; beside it the same step as kv_append_fp8
+    then paged_decode_attn_fp8), on the chosen workload's shapes with
     random E4M3 codes in the pools; beside it the fp16 decode of the same
     shapes (paged_decode_attn) for the ratio. Bytes count one byte per pool
     element."""
@@ -217,6 +218,11 @@ def bench_fp8(args, torch, pa):
 
     def step(i):
         for q, kn, vn, kp, vp in sets[i % R]:
+            pa.paged_decode_attn_append_fp8(q, kn, vn, kp, vp, tables, lens, w.bs, w.scale, ks, vs, out=out,
+                                            workspace=ws)
+
+    def step_two_calls(i):
+        for q, kn, vn, kp, vp in sets[i % R]:
             pa.kv_append_fp8(kn, vn, kp, vp, tables, lens, w.bs, ks, vs)
             pa.paged_decode_attn_fp8(q, kp, vp, tables, lens, w.bs, w.scale, ks, vs, out=out, workspace=ws)
 
@@ -234,6 +240,7 @@ def bench_fp8(args, torch, pa):
         return t0.elapsed_time(t1) / n
 
     ms_per_step = timed(step, args.steps)
+    two_call_ms = timed(step_two_calls, args.steps)
     dec_ms = timed(lambda i: pa.paged_decode_attn_fp8(sets[i % R][i % layers][0], sets[i % R][i % layers][3],
                                                        sets[i % R][i % layers][4], tables, lens, w.bs, w.scale, ks,
                                                        vs, out=out, workspace=ws), args.steps)
@@ -270,6 +277,7 @@ def bench_fp8(args, torch, pa):
                    "head_dim": w.D, "block_size": w.bs, "seq_len_sum": int(w.seq_lens.sum()), "replicas": R},
         "rows_layers_per_s": round(w.B * layers / (ms_per_step * 1e-3), 1),
         "bytes_per_step": launch_bytes * layers,
+        "two_call_ms_per_step": round(two_call_ms, 6),
         "decode_us": round(dec_ms * 1e3, 3),
         "append_us": round(app_ms * 1e3, 3),
         "fp16_decode_us": round(f16_ms * 1e3, 3),

@@ -303,6 +303,23 @@ pa_status paged_decode_attn_fp8(uint16_t *out, const uint16_t *q, const uint8_t 
                                 float v_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * paged_decode_attn_append_fp8 -- kv_append_fp8 followed by
+ * paged_decode_attn_fp8 in one launch, as paged_decode_attn_append is for
+ * fp16 pools: the pools and the output are bit-identical to the two calls'.
+ * The new token's codes are written into the tile in LDS and into the pool
+ * by the workgroup that reads the row's last tile. k_new, v_new: [B][Hkv][D]
+ * fp16, 16-byte aligned, non-null when num_seqs > 0. Arguments, workspace
+ * and errors otherwise as paged_decode_attn_fp8; the preconditions of
+ * kv_append hold.
+ */
+pa_status paged_decode_attn_append_fp8(uint16_t *out, const uint16_t *q, const uint16_t *k_new,
+                                       const uint16_t *v_new, uint8_t *k_pool, uint8_t *v_pool,
+                                       const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                                       float v_scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -24,6 +24,9 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   paged_decode_attn_fp8(q, k_pool, v_pool, block_tables, seq_lens,
                         block_size, scale, k_scale, v_scale, out=None,
                         workspace=None)                    (E4M3 pools)
+  paged_decode_attn_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables,
+                               seq_lens, block_size, scale, k_scale, v_scale,
+                               out=None, workspace=None)  (the two above, fused)
 
 Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16);
 E4M3 pools (uint8 codes, or torch.float8_e4m3fn): k_pool [N][Hkv][D/16][bs][16],
@@ -85,6 +88,8 @@ def lib():
     L.kv_append_fp8.restype = ctypes.c_int
     L.paged_decode_attn_fp8.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float] * 3 + [vp, sz, vp]
     L.paged_decode_attn_fp8.restype = ctypes.c_int
+    L.paged_decode_attn_append_fp8.argtypes = [vp] * 8 + [i32] * 7 + [ctypes.c_float] * 3 + [vp, sz, vp]
+    L.paged_decode_attn_append_fp8.restype = ctypes.c_int
     L.paged_gather_kv.argtypes = [vp] * 6 + [i32] * 6 + [vp]
     L.paged_gather_kv.restype = ctypes.c_int
     _lib = L
@@ -367,5 +372,34 @@ def paged_decode_attn_fp8(q, k_pool, v_pool, block_tables, seq_lens, block_size,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
     )
     _check(st, "paged_decode_attn_fp8")
+    return out
+
+
+def paged_decode_attn_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size, scale,
+                                 k_scale, v_scale, out=None, workspace=None, stream=None):
+    """kv_append_fp8 + paged_decode_attn_fp8 in one launch (same results)."""
+    k_pool, v_pool = _fp8_pool(k_pool, "k_pool"), _fp8_pool(v_pool, "v_pool")
+    N, Hkv, D = _pool_dims_fp8(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+    st = lib().paged_decode_attn_append_fp8(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
+    )
+    _check(st, "paged_decode_attn_append_fp8")
     return out
 

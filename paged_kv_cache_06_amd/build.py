@@ -20,7 +20,7 @@ SOURCES = [
     os.path.join(CSRC, "pagedattn_fp8.hip"),  # E4M3-pool instances of the decode kernel
     os.path.join(CSRC, "blockops.hip"),  # the block operations
 ]
-HEADERS = [os.path.join(CSRC, "decode_kernel.h")]
+HEADERS = [os.path.join(CSRC, "decode_kernel.h"), os.path.join(CSRC, "e4m3.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpagedattn.so")
 

@@ -26,6 +26,7 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "e4m3.h"
 #include "pagedattn.h"
 
 namespace {
@@ -89,25 +90,6 @@ __global__ void __launch_bounds__(64) append_kernel(const uint16_t* __restrict__
 }
 
 // One workgroup per (row, KV head, logical block); thread per (token, channel).
-// fp32 -> E4M3 code (OCP 8-bit float, bias 7, 3 mantissa bits, no
-// infinity): round to nearest, ties to even mantissa; magnitudes from 448 up
-// (infinity included) saturate to 448; NaN gives 0x7f; the sign bit is kept.
-__device__ __forceinline__ unsigned e4m3_rne_sat(float t) {
-    const unsigned u = __float_as_uint(t);
-    const unsigned sign = (u >> 24) & 0x80u;
-    const unsigned a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7fu;          // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;  // |t| >= 448
-    if (a < 0x3c800000u) {                      // |t| < 2^-6: multiples of 2^-9 (the product is exact)
-        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8; 8 is the code of 2^-6
-        return sign | (unsigned)m;
-    }
-    // normal: round the 20 dropped mantissa bits to nearest even; a carry
-    // moves into the exponent, and |t| < 448 keeps the result at most 448
-    const unsigned r = a + 0x7ffffu + ((a >> 20) & 1u);
-    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
-}
-
 // One wave per (row, KV head): each lane quantizes channels lane, lane+64, ...
 // of the new token's K and V (code of x / scale, the quotient correctly
 // rounded in fp32) and stores the bytes into the row's last block.
@@ -130,8 +112,8 @@ __global__ void __launch_bounds__(64) append_fp8_kernel(const uint16_t* __restri
     const _Float16* ks = reinterpret_cast<const _Float16*>(k_new) + ((size_t)b * Hkv + g) * D;
     const _Float16* vs = reinterpret_cast<const _Float16*>(v_new) + ((size_t)b * Hkv + g) * D;
     for (int d = lane; d < D; d += 64) {
-        k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] = (uint8_t)e4m3_rne_sat((float)ks[d] / k_scale);
-        v_pool[(base * D + d) * BS + slot] = (uint8_t)e4m3_rne_sat((float)vs[d] / v_scale);
+        k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] = (uint8_t)pa_e4m3::quantize(ks[d], k_scale);
+        v_pool[(base * D + d) * BS + slot] = (uint8_t)pa_e4m3::quantize(vs[d], v_scale);
     }
 }
 

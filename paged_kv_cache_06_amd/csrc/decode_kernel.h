@@ -38,6 +38,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "e4m3.h"
+
 namespace pa_detail {
 
 // A decode kernel instance and its workgroup size.
@@ -314,8 +316,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
     asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
 }
-__device__ __forceinline__ void st_b128(uint16_t* p, u32x4 v) {
+__device__ __forceinline__ void st_b128(void* p, u32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_u8(void* p, unsigned v) {
+    asm volatile("global_store_byte %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int N) {
@@ -436,7 +441,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int32_t* __restrict__ counters, float* __restrict__ part_ml,
-    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float v_scale) {
+    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float k_scale, float v_scale) {
     using K = Cfg<BS, D, NREP, F8>;
     constexpr int NJ = K::NJ, NC = K::NC, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
     constexpr int E = K::E, G16 = K::G16, TT = K::TT, HALVES = K::HALVES, NJH = K::NJH;
@@ -465,7 +470,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     const int cap = W * BS;
     // V load lane: row (channel) among the instruction's 8, and chunk of G16 tokens (8 chunks per tile)
     const int drow = lane & 7, vc = lane >> 3;
-    const bool append = !F8 && k_new != nullptr;  // fused kv_append (fp16 pools): this step's K/V enter the pool here
+    const bool append = k_new != nullptr;  // fused kv_append: this step's K/V enter the pool here
 
     // ---- tile list: lengths and the prefix count of tiles per row
     for (int r = tid; r < B; r += THREADS) {
@@ -648,20 +653,33 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         const bool tile = P0.has_tile();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mk1 : mk0));
-        if (!F8 && loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
+        // the new token's 16-byte K group `lane` in the tile: instruction (half, group), slot tn % 64
+        auto new_k_slot = [&](int tn) {
+            return reinterpret_cast<u32x4*>(&s_k[buf][((tn >> 6) * NJH + lane) * 512 + (tn & 63) * 8]);
+        };
+        if (loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const int tn = P0.L - 1 - P0.tile * TT;
-            if (lane < D / 8)
-                *reinterpret_cast<u32x4*>(&s_k[buf][lane * 512 + tn * 8]) =
-                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
+            if constexpr (!F8) {
+                if (lane < D / 8) *new_k_slot(tn) = *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
+            } else {  // quantized, one channel per lane and half: byte c%16 of group c/16
+                const _Float16* x = reinterpret_cast<const _Float16*>(&s_kn[buf][0]);
+                uint8_t* kt = reinterpret_cast<uint8_t*>(&s_k[buf][0]) + (tn & 63) * 16;
+#pragma unroll
+                for (int hv = 0; hv < NH; ++hv) {
+                    const int c = hv * 64 + lane;
+                    kt[((tn >> 6) * NJH + (c >> 4)) * 1024 + (c & 15)] = (uint8_t)pa_e4m3::quantize(x[c], k_scale);
+                }
+            }
             wait_lds();
         }
         tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
-        if (!F8 && wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N && lane < D / 8) {
+        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N && lane < D / G16) {
             // fused append: the new token's K into the pool (nothing in this launch reads it back)
             const size_t base = (size_t)P0.enew * Hkv + P0.g;
-            st_b128(k_pool + ((base * (D / 8) + lane) * BS + (P0.L - 1) % BS) * 8,
-                    *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]));
+            const int tn = P0.L - 1 - P0.tile * TT;
+            st_b128(reinterpret_cast<char*>(k_pool) + ((base * (D / G16) + lane) * BS + (P0.L - 1) % BS) * 16,
+                    *new_k_slot(tn));
         }
         if (loader && P1.valid(t_end) && P1.has_tile()) {
             if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
@@ -766,25 +784,45 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             }
             wait_lds();
         }
-        if (F8 && loader && tile && P0.tile * TT + TT > P0.L) {
+        // byte of channel c, tile token tn in an E4M3 V tile: instruction c/8, chunk tn/16, row c%8
+        auto v8_at = [&](int c, int tn) {
+            return reinterpret_cast<uint8_t*>(&s_v[buf][0]) + (c >> 3) * 1024 + ((tn >> 4) * 8 + (c & 7)) * 16 +
+                   (tn & 15);
+        };
+        if (F8 && loader && tile && (P0.tile * TT + TT > P0.L || P0.nw)) {
             // an E4M3 tile past the row's end: its dead slots may hold NaN
             // codes; they are zeroed in LDS here (lane = chunk*8 + row, one
-            // 16-byte unit per instruction), so PV needs no masking
+            // 16-byte unit per instruction), so PV needs no masking; then
+            // the fused append's new token (quantized) goes into its slot
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const u32x4 mask = keep_first_bytes(P0.L - (P0.tile * TT + 16 * vc));
-            char* vt = reinterpret_cast<char*>(&s_v[buf][0]) + 16 * lane;
+            if (P0.tile * TT + TT > P0.L) {
+                const u32x4 mask = keep_first_bytes(P0.L - (P0.tile * TT + 16 * vc));
+                char* vt = reinterpret_cast<char*>(&s_v[buf][0]) + 16 * lane;
 #pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<u32x4*>(vt + jj * 1024) &= mask;
+                for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<u32x4*>(vt + jj * 1024) &= mask;
+            }
+            if (P0.nw) {
+                const int tn = P0.L - 1 - P0.tile * TT;
+                const _Float16* x = reinterpret_cast<const _Float16*>(&s_vn[buf][0]);
+#pragma unroll
+                for (int hv = 0; hv < NH; ++hv)
+                    *v8_at(hv * 64 + lane, tn) = (uint8_t)pa_e4m3::quantize(x[hv * 64 + lane], v_scale);
+            }
             wait_lds();
         }
         tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
-        if (!F8 && wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N) {
+        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N) {
             // fused append: the new token's V into the pool
             const size_t base = (size_t)P0.enew * Hkv + P0.g;
+            const int slot = (P0.L - 1) % BS;
 #pragma unroll
             for (int hv = 0; hv < NH; ++hv) {
                 const int c = hv * 64 + lane;
-                st_u16(v_pool + (base * D + c) * BS + (P0.L - 1) % BS, s_vn[buf][c]);
+                if constexpr (!F8)
+                    st_u16(v_pool + (base * D + c) * BS + slot, s_vn[buf][c]);
+                else
+                    st_u8(reinterpret_cast<uint8_t*>(v_pool) + (base * D + c) * BS + slot,
+                          *v8_at(c, P0.L - 1 - P0.tile * TT));
             }
         }
         if (loader && P2.valid(t_end) && P2.has_tile()) {

@@ -166,7 +166,7 @@ struct PoolFormat {
 constexpr PoolFormat kFp16Pool = {false, 1.0f, 1.0f};
 
 // paged_decode_attn, and with k_new/v_new (non-null) the same launch with
-// kv_append of the step's K/V fused in (fp16 pools only).
+// kv_append of the step's K/V fused in (quantized for E4M3 pools).
 pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_pool, const int32_t* block_tables,
                         const int32_t* seq_lens, const uint16_t* k_new, const uint16_t* v_new, int32_t num_seqs,
                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -177,7 +177,6 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
         return PA_ERR_INVALID_ARG;
     if (!(std::isfinite(fmt.k_scale) && fmt.k_scale > 0.f && std::isfinite(fmt.v_scale) && fmt.v_scale > 0.f))
         return PA_ERR_INVALID_ARG;
-    if (fmt.fp8 && (k_new || v_new)) return PA_ERR_INVALID_ARG;
     const int nrep = num_heads / num_kv_heads;
     DecodeFn fn = fmt.fp8 ? pa_detail::pick_decode_fp8(block_size, head_dim, nrep) : pick_decode(block_size, head_dim, nrep);
     if (!fn) return PA_ERR_UNSUPPORTED;
@@ -199,7 +198,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
     float* part_ml = reinterpret_cast<float*>(ws);
     float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
     float sl2 = scale * fmt.k_scale * 1.4426950408889634f;
-    float vsc = fmt.v_scale;
+    float ksc = fmt.k_scale, vsc = fmt.v_scale;
     int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;
     // Rows are processed kMaxRows at a time (the workgroups keep the rows'
     // lengths in LDS); each launch covers its own rows of every buffer.
@@ -216,7 +215,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
         float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
         float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
         void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
-                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &vsc};
+                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &ksc, &vsc};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
             hipSuccess)
             return PA_ERR_HIP;
@@ -259,6 +258,18 @@ pa_status paged_decode_attn_fp8(uint16_t* out, const uint16_t* q, const uint8_t*
                          nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream, 0,
                          PoolFormat{true, k_scale, v_scale});
+}
+
+pa_status paged_decode_attn_append_fp8(uint16_t* out, const uint16_t* q, const uint16_t* k_new,
+                                       const uint16_t* v_new, uint8_t* k_pool, uint8_t* v_pool,
+                                       const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                                       float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+    return launch_decode(out, q, k_pool, v_pool, block_tables, seq_lens, k_new, v_new, num_seqs, num_heads,
+                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, workspace,
+                         workspace_bytes, stream, 0, PoolFormat{true, k_scale, v_scale});
 }
 
 pa_status paged_decode_attn_append(uint16_t* out, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_masked",
               "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
-              "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8",
+              "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8", "paged_decode_attn_append_fp8",
               "paged_decode_supported"]:
         assert n in names
 
@@ -165,6 +165,16 @@ def test_fp8_calls_reject_bad_arguments_on_host(pa):
     assert dec(D=96) == 2
     assert dec(ws=None) == 4
     assert app(D=120) == 1  # head_dim % 16
+
+    def fused(kn=f, ks=0.5, bs=64, B=4):
+        return L.paged_decode_attn_append_fp8(f, f, kn, f, f, f, f, f, B, 12, 2, 128, bs, 4, 16, fl(0.1), fl(ks),
+                                              fl(0.5), f, 1 << 30, None)
+
+    assert fused(kn=None) == 1
+    assert fused(ks=0.0) == 1
+    assert fused(kn=ctypes.c_void_p((1 << 20) + 8)) == 1  # misaligned k_new
+    assert fused(bs=24) == 2
+    assert fused(B=0) == 0
     assert app(k=None) == 1
     assert app(B=0) == 0  # nothing to do
 

@@ -10,7 +10,10 @@
   path's, with the two scales folded in), for every compiled (block size,
   head dim, group size), lengths around block and tile edges, zero-length
   rows, NaN codes in every dead slot, and rows split over many partitions;
-* an append followed by a decode step on the Qwen2.5-1.5B batch shape.
+* an append followed by a decode step on the Qwen2.5-1.5B batch shape;
+* the fused step (paged_decode_attn_append_fp8) leaves the pools
+  bit-identical to the oracle's append and its output bit-identical to the
+  two calls', for new tokens at every position of a 128-token tile's edges.
 """
 
 import os
@@ -172,3 +175,29 @@ def test_fp8_step_on_qwen_batches(torch, pa, oracle, name):
     ref, _ = oracle.paged_decode_attn_fp8(q, kp, vp, w.tables, w.seq_lens, w.bs, w.scale, ks, vs,
                                           nthreads=NTHREADS)
     assert_close(host(out), ref, f"fp8 step {name}")
+
+
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_fused_fp8_step_equals_two_calls(torch, pa, oracle, bs):
+    # new tokens at the first, 64th, 65th and last slot of a 128-token tile, a block's edges, and L = 1
+    lens = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 4096]
+    w, rng, q, kp, vp = fp8_case(600 + bs, lens, 12, 2, 128, bs)
+    wl.poison_stale(kp, vp, w.tables, w.seq_lens, bs, value=NAN_CODE)
+    kn = (wl.normal_f16(rng, (w.B, 2, 128)).astype(np.float32) * 3).astype(np.float16)
+    vn = wl.normal_f16(rng, (w.B, 2, 128))
+    ks, vs = 0.0625, 0.19
+    say("fused fp8 step", "bs", bs)
+    tt, tl, tq, tkn, tvn = (dev(torch, x) for x in (w.tables, w.seq_lens, q, kn, vn))
+    fk, fv = dev(torch, kp), dev(torch, vp)
+    fused = pa.paged_decode_attn_append_fp8(tq, tkn, tvn, fk, fv, tt, tl, bs, w.scale, ks, vs)
+    ck, cv = dev(torch, kp), dev(torch, vp)
+    pa.kv_append_fp8(tkn, tvn, ck, cv, tt, tl, bs, ks, vs)
+    two = pa.paged_decode_attn_fp8(tq, ck, cv, tt, tl, bs, w.scale, ks, vs)
+    torch.cuda.synchronize()
+    ek, ev = kp.copy(), vp.copy()
+    assert oracle.kv_append_fp8(kn, vn, ek, ev, w.tables, w.seq_lens, bs, ks, vs) == 0
+    assert np.array_equal(host(fk), ek) and np.array_equal(host(fv), ev)
+    assert np.array_equal(host(fused).view(np.uint16), host(two).view(np.uint16))
+    ref, _ = oracle.paged_decode_attn_fp8(q, ek, ev, w.tables, w.seq_lens, bs, w.scale, ks, vs, nthreads=NTHREADS)
+    assert_close(host(fused), ref, f"fused fp8 step bs={bs}")
+
