@@ -635,6 +635,26 @@ def main():
     ms_per_step = time_steps(step)
     two_call_ms_per_step = time_steps(step_two_calls)
 
+    # ---- the same steps replayed from a HIP graph: one capture of a cycle
+    # through the R replicas (R steps), replayed until K steps have run
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(R):
+            step(i)
+    reps = max(1, math.ceil(args.steps / R))
+    for _ in range(max(1, math.ceil(args.warmup / R))):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(reps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms_per_step = g0.elapsed_time(g1) / (reps * R)
+    del graph
+
     # ---- per-launch durations (events around each launch)
     n_k = max(20, min(args.steps, 400))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
@@ -741,6 +761,8 @@ def main():
         "unique_bytes_per_step": unique_step_bytes,
         "two_call_ms_per_step": round(two_call_ms_per_step, 6),
         "two_call_value": round(step_bytes / (two_call_ms_per_step * 1e-3) / 1e9, 2),
+        "graph_ms_per_step": round(graph_ms_per_step, 6),
+        "graph_value": round(step_bytes / (graph_ms_per_step * 1e-3) / 1e9, 2),
         "decode_us": round(dec_b2b_ms * 1e3, 3),
         "decode_us_bracketed": round(dec_ms * 1e3, 3),
         "decode_without_append_us": round(dec_only_b2b_ms * 1e3, 3),
