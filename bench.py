@@ -43,6 +43,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -64,11 +65,18 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_REPS = 10
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and blank lines (a comment edit does not change the kernel)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,8 +25,9 @@
 // merge by the last partition to arrive) is described above decode_kernel.
 //
 // Stale slots and unlisted blocks may hold NaN: scores of tokens past the
-// row's length are replaced (not multiplied) by -inf, and their V halves are
-// zeroed before the dot products.
+// row's length are replaced (not multiplied) by -inf, and their V values are
+// zeroed before the dot products (fp16: in registers; E4M3: in LDS, by the
+// load wave).
 
 #pragma once
 
@@ -422,14 +423,18 @@ struct Cfg {
 // boundaries as well. The query of a unit is loaded into LDS with the K tile
 // of its first position.
 //
-// Layouts: the K tile in LDS is [NJ][64 tokens][8 ch] (lane = token for QK);
-// the V tile is [NJ row blocks][8 chunks][8 rows][8 tokens], loaded so that a
-// load instruction still covers eight whole 128-byte rows of V. PV uses lane =
-// channel: lane ch reads the 8 chunks of its channel's 64 tokens, odd row
-// blocks in the order c^1, which keeps every 16-lane phase of the LDS read on
-// distinct banks. The p vector of a head (fp16, 64 tokens) is broadcast from
-// LDS. A lane thus owns whole output channels: no cross-lane reduction of the
-// output at all.
+// Layouts (fp16 pools, 64-token tiles): the K tile in LDS is [NJ][64
+// tokens][8 ch] (lane = token for QK); the V tile is [NJ row blocks][8
+// chunks][8 rows][8 tokens], loaded so that a load instruction still covers
+// eight whole 128-byte rows of V. PV uses lane = channel: lane ch reads the 8
+// chunks of its channel's 64 tokens, odd row blocks in the order c^1, which
+// keeps every 16-lane phase of the LDS read on distinct banks. The p vector
+// of a head (fp16, one per tile token) is broadcast from LDS. A lane thus
+// owns whole output channels: no cross-lane reduction of the output at all.
+// E4M3 pools, 128-token tiles: the K tile is [2 halves][D/16][64 tokens][16
+// ch] bytes (lane = token of each half); the V tile's bytes sit exactly as an
+// fp16 tile's, each 16-byte unit now 16 tokens of one row, and PV widens each
+// unit to two fp16 chunks.
 //
 // Results: a one-partition row writes fp16 output directly; otherwise the
 // partition writes (max, sum, unnormalised output) with coherent stores and is
