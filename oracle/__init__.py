@@ -66,6 +66,8 @@ def _load(path=None):
     lib.oracle_paged_decode_attn_fp8.argtypes = [f32p, u16p, u16p, u8p, u8p, i32p, i32p] + [i32] * 7 + [
         f32, f32, f32, i32]
     lib.oracle_paged_decode_attn_fp8.restype = ctypes.c_int
+    lib.oracle_kv_copy_blocks_fp8.argtypes = [u8p, u8p, i32p, i32p] + [i32] * 5
+    lib.oracle_kv_copy_blocks_fp8.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_kv_copy_blocks.argtypes = [u16p, u16p, i32p, i32p] + [i32] * 5
@@ -202,6 +204,20 @@ class Oracle:
         assert s.shape == d.shape and s.ndim == 1
         return self.lib.oracle_kv_copy_blocks(
             self._p(kp, ctypes.c_uint16), self._p(vp, ctypes.c_uint16),
+            self._p(s, ctypes.c_int32), self._p(d, ctypes.c_int32),
+            s.size, Hkv, D, bs, N,
+        )
+
+    def kv_copy_blocks_fp8(self, k_pool, v_pool, src, dst):
+        """In-place on uint8 E4M3 pools ([N][Hkv][D/16][bs][16], [N][Hkv][D][bs]); returns the C status."""
+        N, Hkv = k_pool.shape[0], k_pool.shape[1]
+        D, bs = v_pool.shape[2], v_pool.shape[3]
+        assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+        s = np.ascontiguousarray(src, dtype=np.int32)
+        d = np.ascontiguousarray(dst, dtype=np.int32)
+        assert s.shape == d.shape and s.ndim == 1
+        return self.lib.oracle_kv_copy_blocks_fp8(
+            self._p(k_pool, ctypes.c_uint8), self._p(v_pool, ctypes.c_uint8),
             self._p(s, ctypes.c_int32), self._p(d, ctypes.c_int32),
             s.size, Hkv, D, bs, N,
         )

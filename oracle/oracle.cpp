@@ -367,6 +367,29 @@ int oracle_kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src
     return rc;
 }
 
+// The same block copies in FP8 pools (E4M3 codes, K groups of 16
+// channels): a byte copy of every KV head and slot of each block. Same
+// return codes as oracle_kv_copy_blocks.
+int oracle_kv_copy_blocks_fp8(uint8_t *k_pool, uint8_t *v_pool, const int32_t *src, const int32_t *dst, int n,
+                              int Hkv, int D, int bs, int N) {
+    if (n < 0 || Hkv <= 0 || D <= 0 || D % 16 || bs <= 0 || N <= 0) return -1;
+    int rc = 0;
+    for (int i = 0; i < n; ++i) {
+        const int32_t s = src[i], t = dst[i];
+        if (s < 0 || s >= N || t < 0 || t >= N) {
+            rc = -2;
+            continue;
+        }
+        for (int g = 0; g < Hkv; ++g)
+            for (int slot = 0; slot < bs; ++slot)
+                for (int d = 0; d < D; ++d) {
+                    k_pool[k_index8(t, g, slot, d, Hkv, D, bs)] = k_pool[k_index8(s, g, slot, d, Hkv, D, bs)];
+                    v_pool[v_index(t, g, slot, d, Hkv, D, bs)] = v_pool[v_index(s, g, slot, d, Hkv, D, bs)];
+                }
+    }
+    return rc;
+}
+
 // Scatter a prefill group's keys and values into the rows' blocks. The group
 // was run left padded to its widest prompt (width S), so row b's prompt of
 // length P = prompt_lens[b] sits at positions S-P .. S-1 of its [S][D] rows

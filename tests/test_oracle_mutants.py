@@ -43,13 +43,17 @@ MUTANTS = {
         "k_pool[k_index(t, g, slot, d, Hkv, D, bs)] = k_pool[k_index(s, g, slot, d, Hkv, D, bs)];",
         "k_pool[k_index(s, g, slot, d, Hkv, D, bs)] = k_pool[k_index(t, g, slot, d, Hkv, D, bs)];",
     ),
-    "copy_skips_last_slot": ("for (int slot = 0; slot < bs; ++slot)\n                for (int d = 0; d < D; ++d) {",
-                             "for (int slot = 0; slot < bs - 1; ++slot)\n                for (int d = 0; d < D; ++d) {"),
+    "copy_skips_last_slot": ("for (int slot = 0; slot < bs; ++slot)\n                for (int d = 0; d < D; ++d) {\n"
+                             "                    k_pool[k_index(t,",
+                             "for (int slot = 0; slot < bs - 1; ++slot)\n                for (int d = 0; d < D; ++d) {\n"
+                             "                    k_pool[k_index(t,"),
     "scatter_keeps_left_padding": ("const size_t s = (size_t)(S - P + t);", "const size_t s = (size_t)t;"),
     "scatter_slot_off_by_one": ("k_pool[k_index(blk, g, t % bs, d, Hkv, D, bs)] = k_src[i];",
                                 "k_pool[k_index(blk, g, (t + 1) % bs, d, Hkv, D, bs)] = k_src[i];"),
-    "copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)",
-                             "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)"),
+    "copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
+                             "                for (int d = 0; d < D; ++d) {\n                    k_pool[k_index(t,",
+                             "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
+                             "                for (int d = 0; d < D; ++d) {\n                    k_pool[k_index(t,"),
     "fp8_exponent_bias": ("std::ldexp((float)(8 + m), e - 10)", "std::ldexp((float)(8 + m), e - 11)"),
     "fp8_subnormal_scale": ("std::ldexp((float)m, -9)", "std::ldexp((float)m, -10)"),
     "fp8_ties_away_from_zero": ("(dc == db && (c & 1) == 0)", "(dc == db)"),
@@ -61,6 +65,14 @@ MUTANTS = {
     "fp8_v_scaled_by_k_scale": ("v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * v_scale;",
                                 "v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * k_scale;"),
     "fp8_k_group_of_8": ("(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 16 +", "(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 8 +"),
+    "fp8_copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
+                                 "                for (int d = 0; d < D; ++d) {\n                    k_pool[k_index8(t,",
+                                 "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
+                                 "                for (int d = 0; d < D; ++d) {\n                    k_pool[k_index8(t,"),
+    "fp8_copy_direction_swapped": (
+        "k_pool[k_index8(t, g, slot, d, Hkv, D, bs)] = k_pool[k_index8(s, g, slot, d, Hkv, D, bs)];",
+        "k_pool[k_index8(s, g, slot, d, Hkv, D, bs)] = k_pool[k_index8(t, g, slot, d, Hkv, D, bs)];",
+    ),
     "fp8_append_slot_off_by_one": ("k_pool[k_index8(blk, g, pos % bs, d", "k_pool[k_index8(blk, g, (pos + 1) % bs, d"),
     "fp8_append_v_with_k_scale": ("quantize_fp8(v_new[i], v_scale)", "quantize_fp8(v_new[i], k_scale)"),
 }
@@ -88,6 +100,7 @@ FAST_PINS = [
     (pins.test_kv_append_fp8_matches_numpy, {}),
     (pins.test_fp8_attention_equals_fp16_oracle_on_exact_pools, {}),
     (pins.test_fp8_attention_matches_float64_dense, {}),
+    (pins.test_kv_copy_blocks_fp8_matches_numpy, {}),
 ]
 
 

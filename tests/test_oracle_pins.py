@@ -616,3 +616,20 @@ def test_fp8_attention_matches_float64_dense(oracle):
         ref = f64_dense(q[b], kl[b], vl[b], w.scale)
         assert close(got[b], ref, atol=2e-6, rtol=1e-4), b
 
+
+def test_kv_copy_blocks_fp8_matches_numpy(oracle):
+    rng = np.random.default_rng(86)
+    N, Hkv, D, bs = 24, 2, 32, 16
+    kp = wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, Hkv, D, bs))
+    vp = wl.fp8_codes(rng, wl.v_pool_shape(N, Hkv, D, bs))
+    perm = rng.permutation(N)
+    src, dst = perm[:6].astype(np.int32), perm[6:12].astype(np.int32)
+    ek, ev = kp.copy(), vp.copy()
+    ek[dst] = kp[src]
+    ev[dst] = vp[src]
+    assert oracle.kv_copy_blocks_fp8(kp, vp, src, dst) == 0
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)
+    bad = np.int32([N, 3]), np.int32([1, -1])
+    assert oracle.kv_copy_blocks_fp8(kp, vp, *bad) == -2
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)  # both pairs skipped
+
