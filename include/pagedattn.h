@@ -320,6 +320,17 @@ pa_status paged_decode_attn_append_fp8(uint16_t *out, const uint16_t *q, const u
                                        float v_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kv_copy_blocks_fp8 -- kv_copy_blocks for FP8 pools (copy-on-write of
+ * shared E4M3 blocks): block dst[i] of both pools takes block src[i]'s
+ * bytes, every KV head and slot. Same pair rules and errors as
+ * kv_copy_blocks; head_dim % 16 == 0; with num_layers > 1, layer_stride is
+ * in bytes (a multiple of 16, at least N*Hkv*D*block_size).
+ */
+pa_status kv_copy_blocks_fp8(uint8_t *k_pool, uint8_t *v_pool, const int32_t *src, const int32_t *dst,
+                             int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t num_layers, int64_t layer_stride, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -27,6 +27,7 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   paged_decode_attn_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables,
                                seq_lens, block_size, scale, k_scale, v_scale,
                                out=None, workspace=None)  (the two above, fused)
+  kv_copy_blocks_fp8(k_pool, v_pool, src, dst, block_size)   (E4M3 pools)
 
 Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16);
 E4M3 pools (uint8 codes, or torch.float8_e4m3fn): k_pool [N][Hkv][D/16][bs][16],
@@ -84,6 +85,8 @@ def lib():
     L.kv_copy_blocks.restype = ctypes.c_int
     L.kv_scatter_prefill.argtypes = [vp] * 6 + [i32] * 7 + [vp]
     L.kv_scatter_prefill.restype = ctypes.c_int
+    L.kv_copy_blocks_fp8.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
+    L.kv_copy_blocks_fp8.restype = ctypes.c_int
     L.kv_append_fp8.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_float] * 2 + [vp]
     L.kv_append_fp8.restype = ctypes.c_int
     L.paged_decode_attn_fp8.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float] * 3 + [vp, sz, vp]
@@ -402,4 +405,25 @@ def paged_decode_attn_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables, 
     )
     _check(st, "paged_decode_attn_append_fp8")
     return out
+
+
+def kv_copy_blocks_fp8(k_pool, v_pool, src, dst, block_size, stream=None):
+    """kv_copy_blocks for E4M3 pools ([N][Hkv][D/16][bs][16], [N][Hkv][D][bs]
+    bytes, or with a leading layer dimension, every layer copied)."""
+    k_pool, v_pool = _fp8_pool(k_pool, "k_pool"), _fp8_pool(v_pool, "v_pool")
+    layered = k_pool.dim() == 6
+    kp1 = k_pool[0] if layered else k_pool
+    vp1 = v_pool[0] if layered else v_pool
+    N, Hkv, D = _pool_dims_fp8(kp1, vp1, block_size)
+    layers = k_pool.shape[0] if layered else 1
+    if layered and (v_pool.dim() != 5 or v_pool.shape[0] != layers):
+        raise ValueError("k_pool / v_pool must both have the same leading layer dimension")
+    if tuple(src.shape) != tuple(dst.shape) or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D of the same length")
+    st = lib().kv_copy_blocks_fp8(
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(src, "src", torch.int32, 1), _dev(dst, "dst", torch.int32, 1),
+        src.numel(), Hkv, D, block_size, N, layers, ctypes.c_int64(N * Hkv * D * block_size), _stream(stream),
+    )
+    _check(st, "kv_copy_blocks_fp8")
 

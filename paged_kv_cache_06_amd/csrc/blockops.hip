@@ -295,6 +295,16 @@ pa_status kv_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src,
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status kv_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, const int32_t* src, const int32_t* dst,
+                             int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t num_layers, int64_t layer_stride, void* stream) {
+    // the fp16 copy kernel moves 16-byte units: an E4M3 block is Hkv*D*bs bytes, i.e. Hkv*(D/2)*bs halves
+    if (head_dim <= 0 || head_dim % 16 || (num_layers > 1 && layer_stride % 2)) return PA_ERR_INVALID_ARG;
+    return kv_copy_blocks(reinterpret_cast<uint16_t*>(k_pool), reinterpret_cast<uint16_t*>(v_pool), src, dst,
+                          num_pairs, num_kv_heads, head_dim / 2, block_size, num_blocks, num_layers,
+                          layer_stride / 2, stream);
+}
+
 pa_status kv_scatter_prefill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
                              const int32_t* block_tables, const int32_t* prompt_lens, int32_t num_seqs,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
               "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
               "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8", "paged_decode_attn_append_fp8",
+              "kv_copy_blocks_fp8",
               "paged_decode_supported"]:
         assert n in names
 
@@ -175,6 +176,14 @@ def test_fp8_calls_reject_bad_arguments_on_host(pa):
     assert fused(kn=ctypes.c_void_p((1 << 20) + 8)) == 1  # misaligned k_new
     assert fused(bs=24) == 2
     assert fused(B=0) == 0
+
+    def cp8(D=128, layers=1, stride=0, n=4):
+        return L.kv_copy_blocks_fp8(f, f, f, f, n, 2, D, 64, 16, layers, ctypes.c_int64(stride), None)
+
+    assert cp8(D=120) == 1  # head_dim % 16
+    assert cp8(layers=2, stride=16 * 2 * 128 * 64 + 8) == 1  # layer stride not 16-byte aligned
+    assert cp8(layers=2, stride=16 * 2 * 128 * 64 - 16) == 1  # layers would overlap
+    assert cp8(n=0) == 0
     assert app(k=None) == 1
     assert app(B=0) == 0  # nothing to do
 

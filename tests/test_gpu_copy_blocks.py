@@ -8,7 +8,10 @@
   (paged_kv_cache_06_amd.blocks), the device copies, then the step (fused or
   as two calls) leave the pools bit-identical to the oracle's copy and append,
   and the output within |gpu - ref| <= 2e-3 + 1e-2 |ref| of the oracle's
-  attention over the repointed tables.
+  attention over the repointed tables;
+* the same over E4M3 (FP8) pools: kv_copy_blocks_fp8 bit-identical to the
+  oracle's byte copy (one layer and layered pools), and a copy-on-write step
+  through the fused E4M3 launch.
 """
 
 import os
@@ -148,3 +151,63 @@ def test_copy_on_write_then_decode_step(torch, pa, oracle, bs, prefix, fused):
     err = np.abs(got - ref)
     assert not np.isnan(got).any()
     assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"max abs err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_copy_blocks_fp8_bit_exact(torch, pa, oracle, bs):
+    Hkv, D, N = 2, 128, 80
+    rng = np.random.default_rng(300 + bs)
+    kp = wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, Hkv, D, bs))
+    vp = wl.fp8_codes(rng, wl.v_pool_shape(N, Hkv, D, bs))
+    perm = rng.permutation(N)
+    src = np.concatenate([perm[:25], [N, 7]]).astype(np.int32)
+    dst = np.concatenate([perm[25:50], [perm[50], 7]]).astype(np.int32)
+    say("copy blocks fp8", "bs", bs, "pairs", src.size)
+    tk, tv = dev(torch, kp), dev(torch, vp)
+    pa.kv_copy_blocks_fp8(tk, tv, dev(torch, src), dev(torch, dst), bs)
+    torch.cuda.synchronize()
+    ek, ev = kp.copy(), vp.copy()
+    assert oracle.kv_copy_blocks_fp8(ek, ev, src, dst) == -2
+    assert np.array_equal(host(tk), ek) and np.array_equal(host(tv), ev)
+    # layered pools: every layer copied
+    layers = 3
+    kl = np.stack([wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, Hkv, D, bs)) for _ in range(layers)])
+    vl = np.stack([wl.fp8_codes(rng, wl.v_pool_shape(N, Hkv, D, bs)) for _ in range(layers)])
+    s2, d2 = perm[:10].astype(np.int32), perm[10:20].astype(np.int32)
+    tk, tv = dev(torch, kl), dev(torch, vl)
+    pa.kv_copy_blocks_fp8(tk, tv, dev(torch, s2), dev(torch, d2), bs)
+    torch.cuda.synchronize()
+    gk, gv = host(tk), host(tv)
+    for layer in range(layers):
+        ek, ev = kl[layer].copy(), vl[layer].copy()
+        assert oracle.kv_copy_blocks_fp8(ek, ev, s2, d2) == 0
+        assert np.array_equal(gk[layer], ek) and np.array_equal(gv[layer], ev), f"layer {layer}"
+
+
+def test_copy_on_write_then_fused_fp8_step(torch, pa, oracle):
+    bs, prefix = 64, 100
+    tables, lens, N, free, q, kn, vn, _, _, scale = _cow_case(bs, prefix, 4, [300, 1, 64, 129], seed=31)
+    rng = np.random.default_rng(32)
+    kp = wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, 2, 128, bs))
+    vp = wl.fp8_codes(rng, wl.v_pool_shape(N, 2, 128, bs))
+    rc = blocks.refcounts(tables, lens, bs, N)
+    src, dst = blocks.plan_copy_on_write(tables, lens, bs, rc, free)
+    assert src.size == 3
+    ks, vs = 0.125, 0.375
+    say("copy-on-write fp8 step", "copies", src.size)
+    tk, tv = dev(torch, kp), dev(torch, vp)
+    tt, tl = dev(torch, tables), dev(torch, lens)
+    pa.kv_copy_blocks_fp8(tk, tv, dev(torch, src), dev(torch, dst), bs)
+    out = pa.paged_decode_attn_append_fp8(dev(torch, q), dev(torch, kn), dev(torch, vn), tk, tv, tt, tl, bs, scale,
+                                          ks, vs)
+    torch.cuda.synchronize()
+    ek, ev = kp.copy(), vp.copy()
+    assert oracle.kv_copy_blocks_fp8(ek, ev, src, dst) == 0
+    assert oracle.kv_append_fp8(kn, vn, ek, ev, tables, lens, bs, ks, vs) == 0
+    assert np.array_equal(host(tk), ek) and np.array_equal(host(tv), ev)
+    ref, _ = oracle.paged_decode_attn_fp8(q, ek, ev, tables, lens, bs, scale, ks, vs, nthreads=NTHREADS)
+    got = host(out).astype(np.float64)
+    err = np.abs(got - ref)
+    assert not np.isnan(got).any()
+    assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"max abs err {err.max():.3e}"
+
