@@ -66,6 +66,8 @@ def _load(path=None):
     lib.oracle_paged_decode_attn_fp8.argtypes = [f32p, u16p, u16p, u8p, u8p, i32p, i32p] + [i32] * 7 + [
         f32, f32, f32, i32]
     lib.oracle_paged_decode_attn_fp8.restype = ctypes.c_int
+    lib.oracle_kv_scatter_prefill_fp8.argtypes = [u16p, u16p, u8p, u8p, i32p, i32p] + [i32] * 7 + [f32, f32]
+    lib.oracle_kv_scatter_prefill_fp8.restype = ctypes.c_int
     lib.oracle_kv_copy_blocks_fp8.argtypes = [u8p, u8p, i32p, i32p] + [i32] * 5
     lib.oracle_kv_copy_blocks_fp8.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, i32p] + [i32] * 6
@@ -235,6 +237,21 @@ class Oracle:
             self._p(kp, ctypes.c_uint16), self._p(vp, ctypes.c_uint16),
             self._p(t, ctypes.c_int32), self._p(p, ctypes.c_int32),
             B, Hkv, D, bs, W, N, S,
+        )
+
+    def kv_scatter_prefill_fp8(self, k_src, v_src, k_pool, v_pool, tables, prompt_lens, bs, k_scale, v_scale):
+        """In-place: row b's prompt (right-aligned in the [B][Hkv][S][D] group), quantized, into E4M3 blocks."""
+        B, Hkv, S, D = k_src.shape
+        W = tables.shape[1]
+        N = k_pool.shape[0]
+        assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+        t = np.ascontiguousarray(tables, dtype=np.int32)
+        p = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+        return self.lib.oracle_kv_scatter_prefill_fp8(
+            self._p(self._bits(k_src), ctypes.c_uint16), self._p(self._bits(v_src), ctypes.c_uint16),
+            self._p(k_pool, ctypes.c_uint8), self._p(v_pool, ctypes.c_uint8),
+            self._p(t, ctypes.c_int32), self._p(p, ctypes.c_int32),
+            B, Hkv, D, bs, W, N, S, ctypes.c_float(k_scale), ctypes.c_float(v_scale),
         )
 
     def gather_kv(self, k_pool, v_pool, tables, seq_lens, bs, Hkv, D, fill=0):

@@ -429,6 +429,39 @@ int oracle_kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint
     return rc;
 }
 
+// The post-prefill scatter into FP8 pools: as oracle_kv_scatter_prefill,
+// each element stored as quantize_fp8(x, k_scale) (keys) or
+// quantize_fp8(x, v_scale) (values) in the E4M3 layouts. Same skips and
+// return codes; D % 16 == 0.
+int oracle_kv_scatter_prefill_fp8(const uint16_t *k_src, const uint16_t *v_src, uint8_t *k_pool, uint8_t *v_pool,
+                                  const int32_t *block_tables, const int32_t *prompt_lens, int B, int Hkv, int D,
+                                  int bs, int W, int N, int S, float k_scale, float v_scale) {
+    if (!dims_ok(B, Hkv, Hkv, D, bs, W) || D % 16 || N <= 0 || S <= 0) return -1;
+    int rc = 0;
+    for (int b = 0; b < B; ++b) {
+        const int P = prompt_lens[b];
+        if (P <= 0) continue;
+        if (P > S || (int64_t)P > (int64_t)W * bs) {
+            rc = -2;
+            continue;
+        }
+        for (int t = 0; t < P; ++t) {
+            const int32_t blk = block_tables[(size_t)b * W + t / bs];
+            if (blk < 0 || blk >= N) {
+                rc = -2;
+                continue;
+            }
+            for (int g = 0; g < Hkv; ++g)
+                for (int d = 0; d < D; ++d) {
+                    const size_t i = (((size_t)b * Hkv + g) * S + (size_t)(S - P + t)) * D + d;
+                    k_pool[k_index8(blk, g, t % bs, d, Hkv, D, bs)] = quantize_fp8(k_src[i], k_scale);
+                    v_pool[v_index(blk, g, t % bs, d, Hkv, D, bs)] = quantize_fp8(v_src[i], v_scale);
+                }
+        }
+    }
+    return rc;
+}
+
 // Copy each row's first seq_len tokens out of the pool into contiguous
 // [B][Hkv][W*bs][D] arrays, walking the table; positions >= seq_len are left
 // untouched. This is the "read the same blocks" debug path [Paged attention,

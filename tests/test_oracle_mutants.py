@@ -65,6 +65,9 @@ MUTANTS = {
     "fp8_v_scaled_by_k_scale": ("v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * v_scale;",
                                 "v_index(table[t / bs], g, t % bs, d, Hkv, D, bs)]) * k_scale;"),
     "fp8_k_group_of_8": ("(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 16 +", "(size_t)(d / 16)) * (size_t)bs * 16 + (size_t)t * 8 +"),
+    "fp8_scatter_keeps_left_padding": ("const size_t i = (((size_t)b * Hkv + g) * S + (size_t)(S - P + t)) * D + d;",
+                                       "const size_t i = (((size_t)b * Hkv + g) * S + (size_t)t) * D + d;"),
+    "fp8_scatter_v_with_k_scale": ("quantize_fp8(v_src[i], v_scale)", "quantize_fp8(v_src[i], k_scale)"),
     "fp8_copy_first_head_only": ("for (int g = 0; g < Hkv; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
                                  "                for (int d = 0; d < D; ++d) {\n                    k_pool[k_index8(t,",
                                  "for (int g = 0; g < 1; ++g)\n            for (int slot = 0; slot < bs; ++slot)\n"
@@ -101,6 +104,7 @@ FAST_PINS = [
     (pins.test_fp8_attention_equals_fp16_oracle_on_exact_pools, {}),
     (pins.test_fp8_attention_matches_float64_dense, {}),
     (pins.test_kv_copy_blocks_fp8_matches_numpy, {}),
+    (pins.test_kv_scatter_prefill_fp8_reads_back_quantized, {}),
 ]
 
 

@@ -633,3 +633,33 @@ def test_kv_copy_blocks_fp8_matches_numpy(oracle):
     assert oracle.kv_copy_blocks_fp8(kp, vp, *bad) == -2
     assert np.array_equal(kp, ek) and np.array_equal(vp, ev)  # both pairs skipped
 
+
+def test_kv_scatter_prefill_fp8_reads_back_quantized(oracle):
+    # every prompt token, read back through its row's table from the E4M3
+    # pools, is the torch-quantized value of the group's unpadded position;
+    # nothing else in the pools moves
+    rng = np.random.default_rng(87)
+    B, Hkv, D, bs = 4, 2, 32, 16
+    prompts = [5, 16, 0, 37]
+    S = max(prompts)
+    N = sum(wl.blocks_for(P, bs) for P in prompts) + 3
+    w = wl.make_workload("pf8", B, 4, Hkv, D, bs, N, prompts, seed=88, events=5)
+    kp = wl.fp8_codes(rng, wl.k_pool_shape_fp8(N, Hkv, D, bs))
+    vp = wl.fp8_codes(rng, wl.v_pool_shape(N, Hkv, D, bs))
+    k_src = wl.normal_f16(rng, (B, Hkv, S, D))
+    v_src = wl.normal_f16(rng, (B, Hkv, S, D))
+    ks, vs = 0.05, 0.3
+    k0, v0 = kp.copy(), vp.copy()
+    assert oracle.kv_scatter_prefill_fp8(k_src, v_src, kp, vp, w.tables, w.seq_lens, bs, ks, vs) == 0
+    live = wl.live_slot_mask(w.tables, w.seq_lens, bs, N)
+    for b, P in enumerate(prompts):
+        if P == 0:
+            continue
+        k, v = wl.read_row(kp, vp, w.tables[b], P, bs)  # [P][Hkv][D] codes
+        ek = torch_fp8_encode(k_src[b, :, S - P:, :].transpose(1, 0, 2).astype(np.float32) / np.float32(ks))
+        ev = torch_fp8_encode(v_src[b, :, S - P:, :].transpose(1, 0, 2).astype(np.float32) / np.float32(vs))
+        assert np.array_equal(k, ek) and np.array_equal(v, ev), b
+    kd = np.broadcast_to(~live[:, None, None, :, None], kp.shape)
+    vd = np.broadcast_to(~live[:, None, None, :], vp.shape)
+    assert np.array_equal(kp[kd], k0[kd]) and np.array_equal(vp[vd], v0[vd])
+
