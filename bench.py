@@ -384,18 +384,24 @@ def bench_scatter_prefill(args, torch, pa):
     U{16..4096} tokens (the pages' range of prompt lengths), left padded to
     4096, Qwen-shaped (2 KV heads, head_dim 128), block 64, scattered into
     shuffled blocks of a 4,096-block pool; replicas rotated. Bytes per call:
-    every prompt token's K and V read once and written once."""
+    every prompt token's K and V read once and written once. With --kv fp8,
+    kv_scatter_prefill_fp8 into E4M3 pools (one byte written per element)."""
     B, Hkv, D, bs, S = 32, 2, 128, 64, 4096
+    fp8 = args.kv == "fp8"
     rng = np.random.default_rng(19)
     prompts = rng.integers(16, S + 1, size=B).astype(np.int32)
     w = wl.make_workload("scatter", B, 12, Hkv, D, bs, 4096, prompts, seed=19, events=0, append=False)
-    moved = int(prompts.sum()) * Hkv * D * 2 * 2 * 2
+    moved = int(prompts.sum()) * Hkv * D * 2 * (2 + (1 if fp8 else 2))
     group_bytes = B * Hkv * S * D * 2 * 2
     R = args.replicas or max(1, math.ceil((1 << 30) / (group_bytes + 4096 * Hkv * D * bs * 2 * 2)))
     ks0 = torch.from_numpy(wl.normal_f16(rng, (B, Hkv, S, D))).cuda()
     vs0 = torch.from_numpy(wl.normal_f16(rng, (B, Hkv, S, D))).cuda()
-    kp0 = torch.zeros(wl.k_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
-    vp0 = torch.zeros(wl.v_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
+    if fp8:
+        kp0 = torch.zeros(wl.k_pool_shape_fp8(4096, Hkv, D, bs), dtype=torch.uint8, device="cuda")
+        vp0 = torch.zeros(wl.v_pool_shape(4096, Hkv, D, bs), dtype=torch.uint8, device="cuda")
+    else:
+        kp0 = torch.zeros(wl.k_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
+        vp0 = torch.zeros(wl.v_pool_shape(4096, Hkv, D, bs), dtype=torch.float16, device="cuda")
     sets = [(ks0, vs0, kp0, vp0)] + [tuple(t.clone() for t in (ks0, vs0, kp0, vp0)) for _ in range(R - 1)]
     tables = torch.from_numpy(w.tables).cuda()
     plen = torch.from_numpy(prompts).cuda()
@@ -403,7 +409,10 @@ def bench_scatter_prefill(args, torch, pa):
 
     def call(i):
         ks, vs, kp, vp = sets[i % R]
-        pa.kv_scatter_prefill(ks, vs, kp, vp, tables, plen, bs)
+        if fp8:
+            pa.kv_scatter_prefill_fp8(ks, vs, kp, vp, tables, plen, bs, 0.05, 0.05)
+        else:
+            pa.kv_scatter_prefill(ks, vs, kp, vp, tables, plen, bs)
 
     for i in range(args.warmup):
         call(i)
@@ -418,7 +427,7 @@ def bench_scatter_prefill(args, torch, pa):
     ms = t0.elapsed_time(t1) / args.steps
     gbs = moved / (ms * 1e-3) / 1e9
     line = {
-        "metric": "kv_scatter_prefill (post-prefill scatter) achieved HBM GB/s",
+        "metric": f"kv_scatter_prefill{'_fp8' if fp8 else ''} (post-prefill scatter) achieved HBM GB/s",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -428,12 +437,13 @@ def bench_scatter_prefill(args, torch, pa):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16",
+        "dtype": "f16 -> e4m3" if fp8 else "u16",
         "data": "synthetic",
-        "config": {"workload": "scatter_prefill", "rows": B, "padded_len": S, "prompt_tokens": int(prompts.sum()),
+        "config": {"workload": "scatter_prefill", "pool": "e4m3" if fp8 else "f16", "rows": B, "padded_len": S, "prompt_tokens": int(prompts.sum()),
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs, "replicas": R, "bytes_per_call": moved},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "scatter_prefill_kernel",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "scatter_prefill_fp8_kernel" if fp8 else "scatter_prefill_kernel",
                      "bytes_per_launch": moved},
         "device": torch.cuda.get_device_name(0),
     }
@@ -551,6 +561,7 @@ def parse():
                          "paged, contiguous, at masked full width, and at block sizes 16..256; fp8: the step "
                          "over E4M3 pools on --config's shapes")
     ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
+    ap.add_argument("--kv", default="f16", choices=["f16", "fp8"], help="scatter_prefill: pool format")
     return ap.parse_args()
 
 

@@ -266,6 +266,9 @@ pa_status kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint1
  * floating point specification (bias 7, 3 mantissa bits, no infinity, NaN
  * = 0x7f/0xff, largest finite 448) with one fp32 scale for every K element
  * of the pool and one for every V element: element value = code * scale.
+ * Every FP8 call takes the scales finite and within [2^-96, 2^96]
+ * (else PA_ERR_INVALID_ARG): over that range the kernels' quotient x / scale
+ * is the correctly rounded one.
  *   k_pool  [N][Hkv][D/16][block_size][16] bytes (16 channels = 16 bytes,
  *                                                token-minor)
  *   v_pool  [N][Hkv][D][block_size]        bytes (tokens contiguous)
@@ -279,8 +282,8 @@ pa_status kv_scatter_prefill(const uint16_t *k_src, const uint16_t *v_src, uint1
  * rounded to fp32 (one correctly rounded division), then to the nearest
  * code with ties to the even mantissa; magnitudes from 448 up saturate to
  * 448, NaN stays NaN (0x7f) and the sign is kept. Same rows skipped and same
- * preconditions as kv_append. k_scale, v_scale: finite and > 0, else
- * PA_ERR_INVALID_ARG; head_dim % 16 != 0 is PA_ERR_INVALID_ARG.
+ * preconditions as kv_append. k_scale, v_scale: finite, in [2^-96, 2^96],
+ * else PA_ERR_INVALID_ARG; head_dim % 16 != 0 is PA_ERR_INVALID_ARG.
  */
 pa_status kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool, uint8_t *v_pool,
                         const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
@@ -293,8 +296,8 @@ pa_status kv_append_fp8(const uint16_t *k_new, const uint16_t *v_new, uint8_t *k
  * v_scale. Codes are widened to fp16 exactly; k_scale is folded into the
  * score scale and v_scale applied to the output. Arguments, workspace
  * (paged_decode_workspace_size) and errors as paged_decode_attn, plus
- * k_scale, v_scale finite and > 0 (else PA_ERR_INVALID_ARG); k_pool and
- * v_pool 16-byte aligned.
+ * k_scale, v_scale finite and in [2^-96, 2^96] (else PA_ERR_INVALID_ARG);
+ * k_pool and v_pool 16-byte aligned.
  */
 pa_status paged_decode_attn_fp8(uint16_t *out, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
                                 const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
@@ -329,6 +332,22 @@ pa_status paged_decode_attn_append_fp8(uint16_t *out, const uint16_t *q, const u
 pa_status kv_copy_blocks_fp8(uint8_t *k_pool, uint8_t *v_pool, const int32_t *src, const int32_t *dst,
                              int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t num_layers, int64_t layer_stride, void *stream);
+
+/*
+ * kv_scatter_prefill_fp8 -- kv_scatter_prefill into FP8 pools: token t of
+ * row b goes to block block_tables[b][t/bs], slot t%bs, every element
+ * quantized as in kv_append_fp8 (the code of x / scale, k_scale for keys,
+ * v_scale for values), in the E4M3 layouts. Same row and block skips as
+ * kv_scatter_prefill. Host checks: head_dim % 16 == 0 and block_size % 16 ==
+ * 0 (else PA_ERR_INVALID_ARG), scales as for every FP8 call, the staging tile
+ * (max of bs*(D+16) and D*(bs+16) bytes) within 64 KiB (else
+ * PA_ERR_UNSUPPORTED).
+ */
+pa_status kv_scatter_prefill_fp8(const uint16_t *k_src, const uint16_t *v_src, uint8_t *k_pool, uint8_t *v_pool,
+                                 const int32_t *block_tables, const int32_t *prompt_lens, int32_t num_seqs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t num_blocks, int32_t padded_len, float k_scale,
+                                 float v_scale, void *stream);
 
 /*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel

@@ -28,6 +28,8 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
                                seq_lens, block_size, scale, k_scale, v_scale,
                                out=None, workspace=None)  (the two above, fused)
   kv_copy_blocks_fp8(k_pool, v_pool, src, dst, block_size)   (E4M3 pools)
+  kv_scatter_prefill_fp8(k_src, v_src, k_pool, v_pool, block_tables,
+                         prompt_lens, block_size, k_scale, v_scale)
 
 Pool layouts: k_pool [N][Hkv][D/8][bs][8], v_pool [N][Hkv][D][bs] (fp16);
 E4M3 pools (uint8 codes, or torch.float8_e4m3fn): k_pool [N][Hkv][D/16][bs][16],
@@ -85,6 +87,8 @@ def lib():
     L.kv_copy_blocks.restype = ctypes.c_int
     L.kv_scatter_prefill.argtypes = [vp] * 6 + [i32] * 7 + [vp]
     L.kv_scatter_prefill.restype = ctypes.c_int
+    L.kv_scatter_prefill_fp8.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float] * 2 + [vp]
+    L.kv_scatter_prefill_fp8.restype = ctypes.c_int
     L.kv_copy_blocks_fp8.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
     L.kv_copy_blocks_fp8.restype = ctypes.c_int
     L.kv_append_fp8.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_float] * 2 + [vp]
@@ -426,4 +430,24 @@ def kv_copy_blocks_fp8(k_pool, v_pool, src, dst, block_size, stream=None):
         src.numel(), Hkv, D, block_size, N, layers, ctypes.c_int64(N * Hkv * D * block_size), _stream(stream),
     )
     _check(st, "kv_copy_blocks_fp8")
+
+
+def kv_scatter_prefill_fp8(k_src, v_src, k_pool, v_pool, block_tables, prompt_lens, block_size, k_scale, v_scale,
+                           stream=None):
+    """kv_scatter_prefill into E4M3 pools, each element quantized (code of x / scale)."""
+    k_pool, v_pool = _fp8_pool(k_pool, "k_pool"), _fp8_pool(v_pool, "v_pool")
+    N, Hkv, D = _pool_dims_fp8(k_pool, v_pool, block_size)
+    B, Hs, S, Ds = k_src.shape
+    if (Hs, Ds) != (Hkv, D) or tuple(v_src.shape) != (B, Hkv, S, D):
+        raise ValueError(f"k_src / v_src must be [B][{Hkv}][S][{D}]")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(prompt_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and prompt_lens [B]")
+    st = lib().kv_scatter_prefill_fp8(
+        _dev(k_src, "k_src", torch.float16, 4), _dev(v_src, "v_src", torch.float16, 4),
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(prompt_lens, "prompt_lens", torch.int32, 1),
+        B, Hkv, D, block_size, W, N, S, ctypes.c_float(k_scale), ctypes.c_float(v_scale), _stream(stream),
+    )
+    _check(st, "kv_scatter_prefill_fp8")
 

@@ -12,6 +12,8 @@
 //   append_fp8_kernel       kv_append_fp8: the same append into E4M3 (FP8)
 //                           pools, quantizing [PagedAttention, "Checking it
 //                           on a real system": FP8 KV halves bytes per token]
+//   scatter_prefill_fp8_kernel  kv_scatter_prefill_fp8: the same scatter into
+//                           E4M3 pools, quantizing
 //   gather_kernel           paged_gather_kv: the debug path, the blocks a row
 //                           lists copied out contiguously [Paged attention,
 //                           "What changed"]
@@ -34,6 +36,10 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// E4M3 pool scales: finite, in [2^-96, 2^96] (the range in which the kernels'
+// quotient x / scale is exact, see e4m3.h).
+bool fp8_scale_ok(float s) { return std::isfinite(s) && s >= 0x1p-96f && s <= 0x1p96f; }
 
 __device__ __forceinline__ int clamp_block(int blk, int N) {
     return (unsigned)blk < (unsigned)N ? blk : 0;
@@ -98,7 +104,8 @@ __global__ void __launch_bounds__(64) append_fp8_kernel(const uint16_t* __restri
                                                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                         const int32_t* __restrict__ tables,
                                                         const int32_t* __restrict__ seq_lens, int Hkv, int D, int BS,
-                                                        int W, int N, float k_scale, float v_scale) {
+                                                        int W, int N, float k_scale, float v_scale, float k_inv,
+                                                        float v_inv) {
     const int bg = blockIdx.x;
     const int b = bg / Hkv, g = bg % Hkv;
     const int lane = threadIdx.x;
@@ -112,8 +119,9 @@ __global__ void __launch_bounds__(64) append_fp8_kernel(const uint16_t* __restri
     const _Float16* ks = reinterpret_cast<const _Float16*>(k_new) + ((size_t)b * Hkv + g) * D;
     const _Float16* vs = reinterpret_cast<const _Float16*>(v_new) + ((size_t)b * Hkv + g) * D;
     for (int d = lane; d < D; d += 64) {
-        k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] = (uint8_t)pa_e4m3::quantize(ks[d], k_scale);
-        v_pool[(base * D + d) * BS + slot] = (uint8_t)pa_e4m3::quantize(vs[d], v_scale);
+        k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] =
+            (uint8_t)pa_e4m3::quantize(ks[d], k_scale, k_inv);
+        v_pool[(base * D + d) * BS + slot] = (uint8_t)pa_e4m3::quantize(vs[d], v_scale, v_inv);
     }
 }
 
@@ -238,6 +246,81 @@ __global__ void __launch_bounds__(256) scatter_prefill_kernel(
     }
 }
 
+// Post-prefill scatter into E4M3 pools: the same grid as scatter_prefill_kernel
+// (keys or values of one logical block of one row and KV head per
+// workgroup), each element quantized (code of x / scale) on its way through
+// LDS. Keys: codes staged token-major ([token][D + 16] bytes), then written
+// 16 bytes per lane along the slots of each 16-channel group ([D/16][bs][16]).
+// Values: codes staged channel-major ([D][bs + 16] bytes), then written 16
+// slots (16 bytes) per lane along each channel row ([D][bs]), single bytes
+// for the slots past the last whole 16 of a partial block.
+__global__ void __launch_bounds__(256) scatter_prefill_fp8_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, const int32_t* __restrict__ tables, const int32_t* __restrict__ prompt_lens,
+    int Hkv, int D, int BS, int W, int N, int S, float k_scale, float v_scale, float k_inv, float v_inv) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+    const bool vpart = (int)blockIdx.x >= W;
+    const int j = vpart ? blockIdx.x - W : blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int P = prompt_lens[b];
+    const int t0 = j * BS;
+    if (P <= 0 || P > S || (long long)P > (long long)W * BS || t0 >= P) return;
+    const int blk = tables[(size_t)b * W + j];
+    if ((unsigned)blk >= (unsigned)N) return;
+    const int n = min(BS, P - t0);  // tokens of this block
+    const int C = D / 8;             // 16-byte groups of 8 fp16 channels per source token
+    const size_t src0 = (((size_t)b * Hkv + g) * S + (size_t)(S - P + t0)) * D;
+    const size_t dst0 = ((size_t)blk * Hkv + g) * (size_t)D * BS;  // the (block, head) slab, bytes, both pools
+    const uint16_t* src = vpart ? v_src : k_src;
+    const float scale = vpart ? v_scale : k_scale, inv = vpart ? v_inv : k_inv;
+
+    if (!vpart) {  // ---- K: [token][D] -> codes [D/16][bs][16]
+        const int RK = D + 16;  // staging row stride, bytes
+        for (int u = threadIdx.x; u < n * C; u += 256) {
+            const int i = u / C, c = u - i * C;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(src + src0 + (size_t)i * D + 8 * c);
+            const _Float16* h = reinterpret_cast<const _Float16*>(&x);
+            unsigned w0 = 0, w1 = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                w0 |= pa_e4m3::quantize(h[k], scale, inv) << (8 * k);
+                w1 |= pa_e4m3::quantize(h[4 + k], scale, inv) << (8 * k);
+            }
+            *reinterpret_cast<uint2*>(s_raw + i * RK + 8 * c) = make_uint2(w0, w1);
+        }
+        __syncthreads();
+        const int C16 = D / 16;
+        for (int u = threadIdx.x; u < n * C16; u += 256) {
+            const int c = u / n, i = u - c * n;
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(s_raw + i * RK + 16 * c),
+                                        reinterpret_cast<u32x4*>(k_pool + dst0 + ((size_t)c * BS + i) * 16));
+        }
+        return;
+    }
+
+    // ---- V: [token][D] -> codes [D][bs]
+    const int RV = BS + 16;  // staging row stride, bytes
+    for (int u = threadIdx.x; u < n * C; u += 256) {
+        const int i = u / C, c = u - i * C;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + src0 + (size_t)i * D + 8 * c);
+        const _Float16* h = reinterpret_cast<const _Float16*>(&x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            s_raw[(8 * c + k) * RV + i] = (unsigned char)pa_e4m3::quantize(h[k], scale, inv);
+    }
+    __syncthreads();
+    const int n16 = n / 16;  // whole 16-slot groups (16-byte aligned in the pool: BS % 16 == 0)
+    for (int u = threadIdx.x; u < D * n16; u += 256) {
+        const int d = u / n16, q = u - d * n16;
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(s_raw + d * RV + 16 * q),
+                                    reinterpret_cast<u32x4*>(v_pool + dst0 + (size_t)d * BS + 16 * q));
+    }
+    const int rest = n - 16 * n16;
+    for (int u = threadIdx.x; u < D * rest; u += 256) {
+        const int d = u / rest, i = 16 * n16 + (u - d * rest);
+        v_pool[dst0 + (size_t)d * BS + i] = s_raw[d * RV + i];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,14 +350,13 @@ pa_status kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new, uint8_t* k
     if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 || block_size <= 0 ||
         max_blocks_per_seq <= 0 || num_blocks <= 0)
         return PA_ERR_INVALID_ARG;
-    if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
-        return PA_ERR_INVALID_ARG;
+    if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PA_ERR_INVALID_ARG;
     if (num_seqs == 0) return PA_OK;
     if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
     if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     hipLaunchKernelGGL(append_fp8_kernel, dim3(num_seqs * num_kv_heads), dim3(64), 0, (hipStream_t)stream, k_new,
                        v_new, k_pool, v_pool, block_tables, seq_lens, num_kv_heads, head_dim, block_size,
-                       max_blocks_per_seq, num_blocks, k_scale, v_scale);
+                       max_blocks_per_seq, num_blocks, k_scale, v_scale, 1.0f / k_scale, 1.0f / v_scale);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -325,6 +407,31 @@ pa_status kv_scatter_prefill(const uint16_t* k_src, const uint16_t* v_src, uint1
                                                     (unsigned)num_seqs),
                        dim3(256), lds, (hipStream_t)stream, k_src, v_src, k_pool, v_pool, block_tables, prompt_lens,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, padded_len);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status kv_scatter_prefill_fp8(const uint16_t* k_src, const uint16_t* v_src, uint8_t* k_pool, uint8_t* v_pool,
+                                 const int32_t* block_tables, const int32_t* prompt_lens, int32_t num_seqs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t num_blocks, int32_t padded_len, float k_scale,
+                                 float v_scale, void* stream) {
+    if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 || head_dim <= 0 ||
+        head_dim % 16 || block_size <= 0 || block_size % 16 || block_size > 1024 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0 || padded_len <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_src || !v_src || !k_pool || !v_pool || !block_tables || !prompt_lens) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+    // LDS: the larger of the K staging ([bs][D+16] bytes) and the V staging ([D][bs+16] bytes)
+    const size_t lds = std::max<size_t>((size_t)block_size * (head_dim + 16), (size_t)head_dim * (block_size + 16));
+    if (lds > 64 * 1024) return PA_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * 2 > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(scatter_prefill_fp8_kernel, dim3((unsigned)max_blocks_per_seq * 2, (unsigned)num_kv_heads,
+                                                        (unsigned)num_seqs),
+                       dim3(256), lds, (hipStream_t)stream, k_src, v_src, k_pool, v_pool, block_tables, prompt_lens,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, padded_len, k_scale,
+                       v_scale, 1.0f / k_scale, 1.0f / v_scale);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -446,7 +446,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int32_t* __restrict__ counters, float* __restrict__ part_ml,
-    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float k_scale, float v_scale) {
+    float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float k_scale, float v_scale,
+    float k_inv, float v_inv) {
     using K = Cfg<BS, D, NREP, F8>;
     constexpr int NJ = K::NJ, NC = K::NC, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
     constexpr int E = K::E, G16 = K::G16, TT = K::TT, HALVES = K::HALVES, NJH = K::NJH;
@@ -673,7 +674,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
 #pragma unroll
                 for (int hv = 0; hv < NH; ++hv) {
                     const int c = hv * 64 + lane;
-                    kt[((tn >> 6) * NJH + (c >> 4)) * 1024 + (c & 15)] = (uint8_t)pa_e4m3::quantize(x[c], k_scale);
+                    kt[((tn >> 6) * NJH + (c >> 4)) * 1024 + (c & 15)] =
+                        (uint8_t)pa_e4m3::quantize(x[c], k_scale, k_inv);
                 }
             }
             wait_lds();
@@ -811,7 +813,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 const _Float16* x = reinterpret_cast<const _Float16*>(&s_vn[buf][0]);
 #pragma unroll
                 for (int hv = 0; hv < NH; ++hv)
-                    *v8_at(hv * 64 + lane, tn) = (uint8_t)pa_e4m3::quantize(x[hv * 64 + lane], v_scale);
+                    *v8_at(hv * 64 + lane, tn) = (uint8_t)pa_e4m3::quantize(x[hv * 64 + lane], v_scale, v_inv);
             }
             wait_lds();
         }

@@ -28,8 +28,22 @@ __device__ __forceinline__ unsigned rne_sat(float t) {
     return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
 }
 
-// The stored code of an fp16 element x of a pool with scale s: the code of
-// the fp32 quotient x / s (one correctly rounded division).
-__device__ __forceinline__ unsigned quantize(_Float16 x, float s) { return rne_sat((float)x / s); }
+// The correctly rounded fp32 quotient x / s for s in [2^-96, 2^96], given
+// y = RN(1/s) (computed once, on the host): q0 = RN(x*y) is within an ulp,
+// and one correction step with a fused multiply-add (Markstein's:
+// r = x - q0*s, exact, then RN(q0 + r*y)) makes it the correctly rounded
+// quotient. Checked against IEEE division for every finite fp16 x and 30,000
+// scales across that range; zeros keep their sign (the sign of the quotient
+// is x's, s > 0), infinities and NaN pass through.
+__device__ __forceinline__ float quotient(float x, float s, float y) {
+    const float q0 = x * y;
+    const float r = __builtin_fmaf(-q0, s, x);
+    const float q = __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+    return __builtin_isinf(x) ? x : q;
+}
+
+// The stored code of an fp16 element x of a pool with scale s (y = RN(1/s)):
+// the code of the correctly rounded fp32 quotient x / s.
+__device__ __forceinline__ unsigned quantize(_Float16 x, float s, float y) { return rne_sat(quotient((float)x, s, y)); }
 
 }  // namespace pa_e4m3

@@ -175,8 +175,8 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
-    if (!(std::isfinite(fmt.k_scale) && fmt.k_scale > 0.f && std::isfinite(fmt.v_scale) && fmt.v_scale > 0.f))
-        return PA_ERR_INVALID_ARG;
+    auto scale_ok = [&](float x) { return std::isfinite(x) && (fmt.fp8 ? x >= 0x1p-96f && x <= 0x1p96f : x > 0.f); };
+    if (!scale_ok(fmt.k_scale) || !scale_ok(fmt.v_scale)) return PA_ERR_INVALID_ARG;
     const int nrep = num_heads / num_kv_heads;
     DecodeFn fn = fmt.fp8 ? pa_detail::pick_decode_fp8(block_size, head_dim, nrep) : pick_decode(block_size, head_dim, nrep);
     if (!fn) return PA_ERR_UNSUPPORTED;
@@ -198,7 +198,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
     float* part_ml = reinterpret_cast<float*>(ws);
     float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
     float sl2 = scale * fmt.k_scale * 1.4426950408889634f;
-    float ksc = fmt.k_scale, vsc = fmt.v_scale;
+    float ksc = fmt.k_scale, vsc = fmt.v_scale, kinv = 1.0f / fmt.k_scale, vinv = 1.0f / fmt.v_scale;
     int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;
     // Rows are processed kMaxRows at a time (the workgroups keep the rows'
     // lengths in LDS); each launch covers its own rows of every buffer.
@@ -215,7 +215,7 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
         float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
         float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
         void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
-                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &ksc, &vsc};
+                        (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &ksc, &vsc, &kinv, &vinv};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=
             hipSuccess)
             return PA_ERR_HIP;

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
               "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
               "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8", "paged_decode_attn_append_fp8",
-              "kv_copy_blocks_fp8",
+              "kv_copy_blocks_fp8", "kv_scatter_prefill_fp8",
               "paged_decode_supported"]:
         assert n in names
 
@@ -157,7 +157,7 @@ def test_fp8_calls_reject_bad_arguments_on_host(pa):
     def app(ks=0.5, vs=0.5, D=128, k=f, B=4):
         return L.kv_append_fp8(f, f, k, f, f, f, B, 2, D, 64, 4, 16, fl(ks), fl(vs), None)
 
-    for bad in (0.0, -1.0, float("nan"), float("inf")):
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-30, 1e30):  # outside [2^-96, 2^96]
         assert dec(ks=bad) == 1 and dec(vs=bad) == 1
         assert app(ks=bad) == 1 and app(vs=bad) == 1
     assert dec(k=ctypes.c_void_p((1 << 20) + 8)) == 1  # misaligned pool
@@ -184,6 +184,15 @@ def test_fp8_calls_reject_bad_arguments_on_host(pa):
     assert cp8(layers=2, stride=16 * 2 * 128 * 64 + 8) == 1  # layer stride not 16-byte aligned
     assert cp8(layers=2, stride=16 * 2 * 128 * 64 - 16) == 1  # layers would overlap
     assert cp8(n=0) == 0
+
+    def sc8(D=128, bs=64, ks=0.5, B=4):
+        return L.kv_scatter_prefill_fp8(f, f, f, f, f, f, B, 2, D, bs, 4, 16, 300, fl(ks), fl(0.5), None)
+
+    assert sc8(D=120) == 1
+    assert sc8(bs=24) == 1  # block_size % 16
+    assert sc8(ks=-1.0) == 1
+    assert sc8(bs=1024) == 2  # staging tile beyond 64 KiB
+    assert sc8(B=0) == 0
     assert app(k=None) == 1
     assert app(B=0) == 0  # nothing to do
 

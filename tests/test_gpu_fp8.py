@@ -86,7 +86,7 @@ def test_append_fp8_every_half_pattern(torch, pa, oracle):
     allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     kn = allbits.reshape(B, Hkv, D).view(np.float16)
     vn = rng.permutation(allbits).reshape(B, Hkv, D).view(np.float16)
-    for ks, vs in [(1.0, 1.0), (0.0371, 3.5)]:
+    for ks, vs in [(1.0, 1.0), (0.0371, 3.5), (2.0 ** -90, 3.1e25), (float.fromhex("0x1.fffffep95"), 1.7e-27)]:
         say("append fp8, every half pattern, scales", ks, vs)
         tk, tv = dev(torch, kp), dev(torch, vp)
         pa.kv_append_fp8(dev(torch, kn), dev(torch, vn), tk, tv, dev(torch, w.tables), dev(torch, w.seq_lens), bs,
