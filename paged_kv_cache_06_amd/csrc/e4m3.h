@@ -32,9 +32,9 @@ __device__ __forceinline__ unsigned rne_sat(float t) {
 // y = RN(1/s) (computed once, on the host): q0 = RN(x*y) is within an ulp,
 // and one correction step with a fused multiply-add (Markstein's:
 // r = x - q0*s, exact, then RN(q0 + r*y)) makes it the correctly rounded
-// quotient. Checked against IEEE division for every finite fp16 x and 30,000
-// scales across that range; zeros keep their sign (the sign of the quotient
-// is x's, s > 0), infinities and NaN pass through.
+// quotient (the CPU test of this construction compares it with IEEE division
+// for every finite fp16 x across that range of scales); zeros keep their sign
+// (the sign of the quotient is x's, s > 0), infinities and NaN pass through.
 __device__ __forceinline__ float quotient(float x, float s, float y) {
     const float q0 = x * y;
     const float r = __builtin_fmaf(-q0, s, x);
