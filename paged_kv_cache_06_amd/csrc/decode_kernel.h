@@ -59,7 +59,6 @@ namespace {
 
 using pa_detail::DecodeFn;
 
-constexpr int kLanes = 64;
 // Tokens per tile: 64 for fp16 pools, 128 for E4M3 pools, so that a tile is
 // 16 KiB of K and 16 KiB of V at head_dim 128 in either format (the bytes a
 // workgroup keeps in flight set its share of the bandwidth). One lane per
@@ -119,8 +118,6 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
     c = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(b.w), c, false);
     return c;
 }
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Two E4M3 bytes of w (bytes 0-1, or 2-3 with HI) as an fp16 pair, first
 // byte in the low half: exact, every E4M3 value is an fp16 value (the

@@ -1,7 +1,8 @@
 // libpagedattn, decode attention: paged KV-cache decode attention for MI355X
 // (gfx950). The block operations (kv_append, kv_copy_blocks,
-// kv_scatter_prefill, paged_gather_kv) live in blockops.hip; both files build
-// into one library behind the C ABI of include/pagedattn.h.
+// kv_scatter_prefill, paged_gather_kv and their E4M3-pool forms) live in
+// blockops.hip; the files build into one library behind the C ABI of
+// include/pagedattn.h.
 //
 // Sources (page title, section):
 //   [Paged attention]     danielfleming.xyz/writing/inference/paged
