@@ -265,6 +265,7 @@ def bench_fp8(args, torch, pa):
     del sets
     f16_ms = timed(lambda i: pa.paged_decode_attn(base[0], p16[i % R16][0], p16[i % R16][1], tables, lens, w.bs,
                                                    w.scale, out=out, workspace=ws), args.steps)
+    probe_us, probe_bytes = probe_read_us(args, torch, pa, decode_bytes_fp8(w), args.steps)
     launch_bytes = decode_bytes_fp8(w) + append_bytes_fp8(w)
     value = launch_bytes * layers / (ms_per_step * 1e-3) / 1e9
     dec_gbs = decode_bytes_fp8(w) / (dec_ms * 1e-3) / 1e9
@@ -290,6 +291,9 @@ def bench_fp8(args, torch, pa):
         "append_us": round(app_ms * 1e3, 3),
         "fp16_decode_us": round(f16_ms * 1e3, 3),
         "decode_speedup_vs_fp16": round(f16_ms / dec_ms, 3),
+        "probe_read": {"bytes": probe_bytes, "us": round(probe_us, 3),
+                       "GBs": round(probe_bytes / (probe_us * 1e-6) / 1e9, 2),
+                       "decode_over_probe_time": round(dec_ms * 1e3 / probe_us, 3)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(dec_gbs, 2),
@@ -304,6 +308,37 @@ def bench_fp8(args, torch, pa):
     }
     print(json.dumps(line), flush=True)
     copy_calibration(args, torch)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def probe_read_us(args, torch, pa, nbytes, n):
+    """Back-to-back launches of the streaming-read probe over nbytes (rounded
+    up to 16), rotating replicas of ~1 GiB in total like the decode; returns
+    (us per launch, bytes)."""
+    nbytes = (nbytes + 15) // 16 * 16
+    R = max(1, math.ceil((1 << 30) / nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    for i in range(max(args.warmup, 1)):
+        pa.probe_read(bufs[i % R], sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        pa.probe_read(bufs[i % R], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3, nbytes
 
 
 def copy_calibration(args, torch):
@@ -707,6 +742,9 @@ def main():
     dec_only_b2b_ms = back_to_back(lambda q, kn, vn, kp, vp: pa.paged_decode_attn(
         q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws))
 
+    # ---- a plain streaming read of the same byte count (the achievable at this size)
+    probe_us, probe_bytes = probe_read_us(args, torch, pa, decode_bytes(w, unique=True) + append_bytes(w), n_k)
+
     launch_bytes = decode_bytes(w) + append_bytes(w)
     unique_launch_bytes = decode_bytes(w, unique=True) + append_bytes(w)
     step_bytes = launch_bytes * layers
@@ -725,15 +763,19 @@ def main():
         kp_h = sets[0][0][3].cpu().numpy()
         vp_h = sets[0][0][4].cpu().numpy()
         q_h, kn_h, vn_h = (sets[0][0][j].cpu().numpy() for j in range(3))
-        reps, t_used = 0, 0.0
-        start = time.perf_counter()
-        while True:
-            orc.kv_append(kn_h, vn_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs)
-            orc.paged_decode_attn(q_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs, w.scale, nthreads=threads)
-            reps += 1
-            t_used = time.perf_counter() - start
-            if t_used + t_used / reps > args.cpu_seconds:  # the next repetition would pass the bound
-                break
+        def sample(nthreads, seconds):
+            reps, t_used = 0, 0.0
+            start = time.perf_counter()
+            while True:
+                orc.kv_append(kn_h, vn_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs)
+                orc.paged_decode_attn(q_h, kp_h, vp_h, w.tables, w.seq_lens, w.bs, w.scale, nthreads=nthreads)
+                reps += 1
+                t_used = time.perf_counter() - start
+                if t_used + t_used / reps > seconds:  # the next repetition would pass the bound
+                    return reps, t_used
+
+        reps, t_used = sample(threads, args.cpu_seconds * 0.75)
+        reps1, t_used1 = sample(1, args.cpu_seconds * 0.25)
         per_layer_s = t_used / reps
         cpu = {
             "value": round((decode_bytes(w) + append_bytes(w)) / per_layer_s / 1e9, 4),
@@ -743,6 +785,9 @@ def main():
             "sample": f"{reps} x (kv_append + paged_decode_attn) of layer 0 of the same workload "
                       f"({w.B} rows), {threads} threads, {t_used:.2f} s",
             "rows_layers_per_s": round(w.B / per_layer_s, 2),
+            "single_thread_value": round((decode_bytes(w) + append_bytes(w)) / (t_used1 / reps1) / 1e9, 4),
+            "single_thread_sample": f"{reps1} x the same on 1 thread, {t_used1:.2f} s",
+            "cpu_model": cpu_model(),
         }
 
     cfg = {
@@ -797,6 +842,9 @@ def main():
             "bytes_per_launch": unique_launch_bytes,
             "logical_GBs": round(dec_gbs, 2),
         },
+        "probe_read": {"bytes": probe_bytes, "us": round(probe_us, 3),
+                       "GBs": round(probe_bytes / (probe_us * 1e-6) / 1e9, 2),
+                       "decode_over_probe_time": round(dec_b2b_ms * 1e3 / probe_us, 3)},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }

@@ -350,6 +350,17 @@ pa_status kv_scatter_prefill_fp8(const uint16_t *k_src, const uint16_t *v_src, u
                                  float v_scale, void *stream);
 
 /*
+ * pa_probe_read -- measurement aid, not part of the decode path: reads
+ * `bytes` bytes of device memory at `src` once (16 bytes per lane,
+ * grid-stride, non-temporal), so that the time of a plain read of a byte
+ * count (launch and ramp included) can be set beside a kernel that reads
+ * that many bytes. sink: device uint32 [num_workgroups], overwritten with
+ * values of no meaning. src 16-byte aligned, bytes a positive multiple of 16,
+ * num_workgroups > 0 (else PA_ERR_INVALID_ARG).
+ */
+pa_status pa_probe_read(const void *src, size_t bytes, uint32_t *sink, int32_t num_workgroups, void *stream);
+
+/*
  * paged_gather_kv -- debug path that reads the same blocks the decode kernel
  * reads and writes them out contiguously [Paged attention, "What changed":
  * the block machinery was first checked through a path that reads the same

@@ -89,6 +89,8 @@ def lib():
     L.kv_scatter_prefill.restype = ctypes.c_int
     L.kv_scatter_prefill_fp8.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float] * 2 + [vp]
     L.kv_scatter_prefill_fp8.restype = ctypes.c_int
+    L.pa_probe_read.argtypes = [vp, sz, vp, i32, vp]
+    L.pa_probe_read.restype = ctypes.c_int
     L.kv_copy_blocks_fp8.argtypes = [vp] * 4 + [i32] * 6 + [ctypes.c_int64, vp]
     L.kv_copy_blocks_fp8.restype = ctypes.c_int
     L.kv_append_fp8.argtypes = [vp] * 6 + [i32] * 6 + [ctypes.c_float] * 2 + [vp]
@@ -450,4 +452,16 @@ def kv_scatter_prefill_fp8(k_src, v_src, k_pool, v_pool, block_tables, prompt_le
         B, Hkv, D, block_size, W, N, S, ctypes.c_float(k_scale), ctypes.c_float(v_scale), _stream(stream),
     )
     _check(st, "kv_scatter_prefill_fp8")
+
+
+def probe_read(buf, sink, num_workgroups=2048, stream=None):
+    """Measurement aid: read every byte of `buf` (a contiguous GPU tensor) once
+    (pa_probe_read); `sink` is a uint32 GPU tensor of num_workgroups words."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink.numel() < num_workgroups:
+        raise ValueError("sink must hold num_workgroups words")
+    st = lib().pa_probe_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                             _dev(sink, "sink", torch.int32), num_workgroups, _stream(stream))
+    _check(st, "pa_probe_read")
 

@@ -321,6 +321,30 @@ __global__ void __launch_bounds__(256) scatter_prefill_fp8_kernel(
     }
 }
 
+// Streaming-read probe: every 16-byte unit of the buffer read once, in
+// coalesced grid-stride order, folded into one XOR per lane so the loads are
+// not dropped; one word per workgroup is written. The bandwidth a plain read
+// of a given byte count reaches, launch and ramp included: the reference a
+// kernel that reads that many bytes can be held against.
+__global__ void __launch_bounds__(256) probe_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    constexpr int kU = 4;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (kU - 1) * stride < n16; i += kU * stride) {
+        u32x4 x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) x[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= x[u];
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(&src[i]);
+    const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    // keep the loads live: one store per workgroup (the XOR of lane 0; its value does not matter)
+    if (threadIdx.x == 0) sink[blockIdx.x] = v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +456,13 @@ pa_status kv_scatter_prefill_fp8(const uint16_t* k_src, const uint16_t* v_src, u
                        dim3(256), lds, (hipStream_t)stream, k_src, v_src, k_pool, v_pool, block_tables, prompt_lens,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, padded_len, k_scale,
                        v_scale, 1.0f / k_scale, 1.0f / v_scale);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 || !aligned16(src) || num_workgroups <= 0) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)num_workgroups), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const u32x4*>(src), bytes / 16, sink);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
               "paged_decode_workspace_size",
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
               "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8", "paged_decode_attn_append_fp8",
-              "kv_copy_blocks_fp8", "kv_scatter_prefill_fp8",
+              "kv_copy_blocks_fp8", "kv_scatter_prefill_fp8", "pa_probe_read",
               "paged_decode_supported"]:
         assert n in names
 
@@ -195,6 +195,15 @@ def test_fp8_calls_reject_bad_arguments_on_host(pa):
     assert sc8(B=0) == 0
     assert app(k=None) == 1
     assert app(B=0) == 0  # nothing to do
+
+
+def test_probe_rejects_bad_arguments_on_host(pa):
+    L = pa.lib()
+    f = FAKE
+    assert L.pa_probe_read(None, 1024, f, 4, None) == 1
+    assert L.pa_probe_read(f, 1000, f, 4, None) == 1  # not a multiple of 16
+    assert L.pa_probe_read(ctypes.c_void_p((1 << 20) + 4), 1024, f, 4, None) == 1
+    assert L.pa_probe_read(f, 1024, f, 0, None) == 1
 
 
 def test_copy_blocks_rejects_bad_arguments_on_host(pa):
