@@ -689,14 +689,15 @@ def main():
     ms_per_step = time_steps(step)
     two_call_ms_per_step = time_steps(step_two_calls)
 
-    # ---- the same steps replayed from a HIP graph: one capture of a cycle
-    # through the R replicas (R steps), replayed until K steps have run
+    # ---- the same steps replayed from a HIP graph: one capture of G = min(R, K)
+    # consecutive steps (through G replicas), replayed until K steps have run
+    G = min(R, args.steps)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for i in range(R):
+        for i in range(G):
             step(i)
-    reps = max(1, math.ceil(args.steps / R))
-    for _ in range(max(1, math.ceil(args.warmup / R))):
+    reps = max(1, math.ceil(args.steps / G))
+    for _ in range(max(1, math.ceil(args.warmup / G))):
         graph.replay()
     torch.cuda.synchronize()
     g0 = torch.cuda.Event(enable_timing=True)
@@ -706,7 +707,7 @@ def main():
         graph.replay()
     g1.record()
     torch.cuda.synchronize()
-    graph_ms_per_step = g0.elapsed_time(g1) / (reps * R)
+    graph_ms_per_step = g0.elapsed_time(g1) / (reps * G)
     del graph
 
     # ---- per-launch durations (events around each launch)
