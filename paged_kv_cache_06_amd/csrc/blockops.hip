@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(64) append_fp8_kernel(const uint16_t* __restri
     const _Float16* vs = reinterpret_cast<const _Float16*>(v_new) + ((size_t)b * Hkv + g) * D;
     for (int d = lane; d < D; d += 64) {
         k_pool[((base * (D / 16) + d / 16) * BS + slot) * 16 + d % 16] =
-            (uint8_t)pa_e4m3::quantize(ks[d], k_scale, k_inv);
-        v_pool[(base * D + d) * BS + slot] = (uint8_t)pa_e4m3::quantize(vs[d], v_scale, v_inv);
+            (uint8_t)pa_e4m3::quantize2(ks[d], ks[d], k_scale, k_inv);
+        v_pool[(base * D + d) * BS + slot] = (uint8_t)pa_e4m3::quantize2(vs[d], vs[d], v_scale, v_inv);
     }
 }
 
@@ -281,9 +281,9 @@ __global__ void __launch_bounds__(256) scatter_prefill_fp8_kernel(
             const _Float16* h = reinterpret_cast<const _Float16*>(&x);
             unsigned w0 = 0, w1 = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                w0 |= pa_e4m3::quantize(h[k], scale, inv) << (8 * k);
-                w1 |= pa_e4m3::quantize(h[4 + k], scale, inv) << (8 * k);
+            for (int k = 0; k < 2; ++k) {
+                w0 |= pa_e4m3::quantize2(h[2 * k], h[2 * k + 1], scale, inv) << (16 * k);
+                w1 |= pa_e4m3::quantize2(h[4 + 2 * k], h[5 + 2 * k], scale, inv) << (16 * k);
             }
             *reinterpret_cast<uint2*>(s_raw + i * RK + 8 * c) = make_uint2(w0, w1);
         }
@@ -304,8 +304,11 @@ __global__ void __launch_bounds__(256) scatter_prefill_fp8_kernel(
         const u32x4 x = *reinterpret_cast<const u32x4*>(src + src0 + (size_t)i * D + 8 * c);
         const _Float16* h = reinterpret_cast<const _Float16*>(&x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            s_raw[(8 * c + k) * RV + i] = (unsigned char)pa_e4m3::quantize(h[k], scale, inv);
+        for (int k = 0; k < 8; k += 2) {
+            const unsigned w = pa_e4m3::quantize2(h[k], h[k + 1], scale, inv);
+            s_raw[(8 * c + k) * RV + i] = (unsigned char)(w & 0xffu);
+            s_raw[(8 * c + k + 1) * RV + i] = (unsigned char)(w >> 8);
+        }
     }
     __syncthreads();
     const int n16 = n / 16;  // whole 16-slot groups (16-byte aligned in the pool: BS % 16 == 0)

@@ -668,11 +668,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             } else {  // quantized, one channel per lane and half: byte c%16 of group c/16
                 const _Float16* x = reinterpret_cast<const _Float16*>(&s_kn[buf][0]);
                 uint8_t* kt = reinterpret_cast<uint8_t*>(&s_k[buf][0]) + (tn & 63) * 16;
+                const unsigned w = pa_e4m3::quantize2(x[lane], x[NH > 1 ? 64 + lane : lane], k_scale, k_inv);
 #pragma unroll
                 for (int hv = 0; hv < NH; ++hv) {
                     const int c = hv * 64 + lane;
-                    kt[((tn >> 6) * NJH + (c >> 4)) * 1024 + (c & 15)] =
-                        (uint8_t)pa_e4m3::quantize(x[c], k_scale, k_inv);
+                    kt[((tn >> 6) * NJH + (c >> 4)) * 1024 + (c & 15)] = (uint8_t)(w >> (8 * hv));
                 }
             }
             wait_lds();
@@ -808,9 +808,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             if (P0.nw) {
                 const int tn = P0.L - 1 - P0.tile * TT;
                 const _Float16* x = reinterpret_cast<const _Float16*>(&s_vn[buf][0]);
+                const unsigned w = pa_e4m3::quantize2(x[lane], x[NH > 1 ? 64 + lane : lane], v_scale, v_inv);
 #pragma unroll
-                for (int hv = 0; hv < NH; ++hv)
-                    *v8_at(hv * 64 + lane, tn) = (uint8_t)pa_e4m3::quantize(x[hv * 64 + lane], v_scale, v_inv);
+                for (int hv = 0; hv < NH; ++hv) *v8_at(hv * 64 + lane, tn) = (uint8_t)(w >> (8 * hv));
             }
             wait_lds();
         }

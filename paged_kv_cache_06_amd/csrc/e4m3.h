@@ -1,6 +1,7 @@
-// e4m3.h: fp32 -> E4M3 (FP8) code, the quantizer of every append into an
-// E4M3 pool (kv_append_fp8 in blockops.hip, the fused append in
-// decode_kernel.h), so that both store the same byte for the same input.
+// e4m3.h: fp16 -> E4M3 (FP8) codes, the quantizer of every write into an
+// E4M3 pool (kv_append_fp8 and kv_scatter_prefill_fp8 in blockops.hip, the
+// fused append in decode_kernel.h), so that all store the same byte for the
+// same input.
 // Internal to libpagedattn.
 
 #pragma once
@@ -8,25 +9,6 @@
 #include <hip/hip_runtime.h>
 
 namespace pa_e4m3 {
-
-// fp32 -> E4M3 code (OCP 8-bit float, bias 7, 3 mantissa bits, no
-// infinity): round to nearest, ties to even mantissa; magnitudes from 448 up
-// (infinity included) saturate to 448; NaN gives 0x7f; the sign bit is kept.
-__device__ __forceinline__ unsigned rne_sat(float t) {
-    const unsigned u = __float_as_uint(t);
-    const unsigned sign = (u >> 24) & 0x80u;
-    const unsigned a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7fu;          // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;  // |t| >= 448
-    if (a < 0x3c800000u) {                      // |t| < 2^-6: multiples of 2^-9 (the product is exact)
-        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8; 8 is the code of 2^-6
-        return sign | (unsigned)m;
-    }
-    // normal: round the 20 dropped mantissa bits to nearest even; a carry
-    // moves into the exponent, and |t| < 448 keeps the result at most 448
-    const unsigned r = a + 0x7ffffu + ((a >> 20) & 1u);
-    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
-}
 
 // The correctly rounded fp32 quotient x / s for s in [2^-96, 2^96], given
 // y = RN(1/s) (computed once, on the host): q0 = RN(x*y) is within an ulp,
@@ -42,8 +24,23 @@ __device__ __forceinline__ float quotient(float x, float s, float y) {
     return __builtin_isinf(x) ? x : q;
 }
 
-// The stored code of an fp16 element x of a pool with scale s (y = RN(1/s)):
-// the code of the correctly rounded fp32 quotient x / s.
-__device__ __forceinline__ unsigned quantize(_Float16 x, float s, float y) { return rne_sat(quotient((float)x, s, y)); }
+// The stored codes of two fp16 elements a, b of a pool with scale s
+// (y = RN(1/s)), byte 0 for a and byte 1 for b: E4M3 (OCP 8-bit float, bias
+// 7, 3 mantissa bits, no infinity) of the correctly rounded fp32 quotients
+// x / s, rounded to nearest with ties to the even mantissa by the hardware
+// converter (v_cvt_pk_fp8_f32); magnitudes from 448 up (infinity included)
+// are clamped to 448 first, so the converter's own result past the largest
+// code never matters; a NaN quotient gives 0x7f; signs are kept (a negative
+// value that rounds to zero gives 0x80). The GPU tests compare the codes of
+// every fp16 bit pattern with the oracle's.
+__device__ __forceinline__ unsigned quantize2(_Float16 a, _Float16 b, float s, float y) {
+    const float qa = quotient((float)a, s, y), qb = quotient((float)b, s, y);
+    unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(__builtin_fmaxf(qa, -448.0f), 448.0f),
+                                                           __builtin_fminf(__builtin_fmaxf(qb, -448.0f), 448.0f),
+                                                           0, false) & 0xffffu;
+    if (__builtin_isnan(qa)) w = (w & 0xff00u) | 0x7fu;
+    if (__builtin_isnan(qb)) w = (w & 0x00ffu) | 0x7f00u;
+    return w;
+}
 
 }  // namespace pa_e4m3
