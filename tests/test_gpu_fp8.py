@@ -201,3 +201,26 @@ def test_fused_fp8_step_equals_two_calls(torch, pa, oracle, bs):
     ref, _ = oracle.paged_decode_attn_fp8(q, ek, ev, w.tables, w.seq_lens, bs, w.scale, ks, vs, nthreads=NTHREADS)
     assert_close(host(fused), ref, f"fused fp8 step bs={bs}")
 
+
+
+def test_fused_fp8_step_more_rows_than_one_launch_takes(torch, pa, oracle):
+    # 1100 short rows, some empty: the host runs the kernel over several row
+    # ranges, each with its own slice of every buffer (the appends included)
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(0, 300, size=1100)]
+    lens[0] = lens[517] = lens[1099] = 0
+    w, rng, q, kp, vp = fp8_case(700, lens, 4, 2, 64, 16)
+    kn = wl.normal_f16(rng, (w.B, 2, 64))
+    vn = wl.normal_f16(rng, (w.B, 2, 64))
+    ks, vs = 0.3, 0.6
+    say("fused fp8 step, 1100 rows")
+    tk, tv = dev(torch, kp), dev(torch, vp)
+    out = pa.paged_decode_attn_append_fp8(dev(torch, q), dev(torch, kn), dev(torch, vn), tk, tv, dev(torch, w.tables),
+                                          dev(torch, w.seq_lens), 16, w.scale, ks, vs)
+    torch.cuda.synchronize()
+    assert oracle.kv_append_fp8(kn, vn, kp, vp, w.tables, w.seq_lens, 16, ks, vs) == 0
+    assert np.array_equal(host(tk), kp) and np.array_equal(host(tv), vp)
+    ref, _ = oracle.paged_decode_attn_fp8(q, kp, vp, w.tables, w.seq_lens, 16, w.scale, ks, vs, nthreads=NTHREADS)
+    got = host(out)
+    assert np.all(got[[0, 517, 1099]].view(np.uint16) == 0)
+    assert_close(got, ref, "fused fp8 step, 1100 rows")
