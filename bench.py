@@ -22,8 +22,16 @@ append's reads and writes) divided by the measured time per step. The
 duration, measured with HIP events on the launch stream around launches
 issued back to back (events bracketing each single launch add a few
 microseconds of their own; that figure is `decode_us_bracketed`), against
-8 TB/s. `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+8 TB/s. `graph_ms_per_step` is the same steps replayed from a HIP graph.
+`probe_read` times a plain streaming read of the same byte count
+(pa_probe_read), the ceiling any kernel reading those bytes meets at that
+size. `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload, on the host's threads and on one thread.
+
+Other modes (`--op`): fp8 (the step over E4M3 pools), contrast (the mixed
+batch paged, contiguous, at masked full width and at block sizes 16..256),
+copy_blocks (copy-on-write block copies), scatter_prefill (the post-prefill
+scatter, `--kv fp8` for E4M3 pools).
 
 `roofline.traffic` is the decode kernel's HBM bytes per launch from two
 rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this same script with
@@ -31,7 +39,7 @@ rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this same script with
 copy of known size in the same run. `--pmc-summary FETCH_DIR WRITE_DIR`
 turns those runs into profiles/decode_kernel_<workload>_traffic.txt; the
 figure is reported only while the kernel source still has the hash recorded
-there, else null.
+there (code, comments excluded), else null.
 """
 
 from __future__ import annotations
