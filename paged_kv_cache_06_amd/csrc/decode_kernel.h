@@ -963,7 +963,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     // their loads in flight together (running max, rescaled sums).
     constexpr int NC4 = NREP * D / 4;
     constexpr int CPT = (NC4 + THREADS - 1) / THREADS;  // chunks per thread
-    constexpr int MB = CPT == 1 ? 16 : 8;               // partitions per round trip
+    constexpr int MB = 8;                               // partitions per round trip
     for (int e = 0; e < npend; ++e) {
         const int np = __builtin_amdgcn_readfirstlane(s_pend_np[e]);
         if (np <= 0) continue;
