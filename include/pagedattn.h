@@ -115,7 +115,8 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
  * ceil(W*block_size/64) being the number of 64-token tiles of a full row,
  * rounded up to 256 bytes, then the per-(row, KV head) int32 arrival counters
  * of the split-sequence reduction, rounded up to 256 bytes. The value never
- * decreases when any argument grows.
+ * decreases when any argument grows. The same size serves the E4M3-pool
+ * calls (their 128-token tiles give at most as many partitions).
  * Returns 0 for invalid sizes.
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
