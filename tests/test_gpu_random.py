@@ -1,8 +1,9 @@
-"""Seeded random parity sweep through the C ABI: 48 cases, each drawing a
-batch size, group shape (Hq, Hkv), head dim, block size, pool format (fp16 or
-E4M3), call form (two calls or the fused step), a length mix (uniform,
-ragged with one long row, or mostly short with empty rows) and a block-table
-history (allocation churn before the tables are built). Dead slots hold NaN
+"""Seeded random parity sweep through the C ABI: 48 cases (the environment
+variable PA_RANDOM_CASES sets another count), each drawing a batch size,
+group shape (Hq, Hkv), head dim, block size, pool format (fp16 or E4M3),
+call form (two calls or the fused step), a length mix (uniform, ragged with
+one long row, or mostly short with empty rows) and a block-table history
+(allocation churn before the tables are built). Dead slots hold NaN
 (fp16) or NaN codes (E4M3). Every case checks the pools bit-exactly against
 the oracle's append and the output within |gpu - ref| <= 2e-3 + 1e-2 |ref|
 of the oracle's attention.
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 ATOL, RTOL = 2e-3, 1e-2
 NTHREADS = min(16, os.cpu_count() or 1)
-CASES = 48
+CASES = int(os.environ.get("PA_RANDOM_CASES", "48"))  # seeds 0 .. CASES-1; the default keeps the suite short
 
 
 @pytest.fixture(scope="module")
