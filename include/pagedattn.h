@@ -27,7 +27,8 @@
  * ---------------------------------------------------------------------------
  *  - All data pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
  *    owned by the caller. The library allocates nothing and keeps no state
- *    between calls except a per-device cache of the compute-unit count.
+ *    between calls except per-device caches of the compute-unit count and
+ *    of each decode kernel's resident workgroups per compute unit.
  *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *    enqueues work on it and returns; there is no host synchronisation and
