@@ -38,6 +38,7 @@ v_pool [N][Hkv][D][bs].
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -166,7 +167,8 @@ def paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, blo
 
 
 def new_workspace(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, device="cuda"):
-    """A zeroed workspace (int8 tensor) of the size paged_decode_attn needs."""
+    """A zeroed workspace (uint8 tensor) of the size paged_decode_attn needs
+    (the fill kernel runs on torch's current stream)."""
     n = paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     paged_decode_workspace_init(ws)
@@ -177,6 +179,27 @@ def paged_decode_workspace_init(workspace, stream=None):
     st = lib().paged_decode_workspace_init(_dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                            _stream(stream))
     _check(st, "paged_decode_workspace_init")
+
+
+def _on(stream):
+    """Context in which a call's own tensors are made: torch's allocator then
+    ties their memory to the call's stream (so it is not handed out again
+    while the call may still use it) and their fill kernels run on it, ahead
+    of the call."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _new_on(stream, shape, dtype, device, zero=False):
+    with _on(stream):
+        return (torch.zeros if zero else torch.empty)(shape, dtype=dtype, device=device)
+
+
+def _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, device, stream):
+    """The caller's workspace, or a zeroed temporary one made on the call's stream."""
+    if workspace is not None:
+        return workspace
+    with _on(stream):
+        return new_workspace(B, Hq, Hkv, D, block_size, W, device=device)
 
 
 def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, out=None, workspace=None,
@@ -190,9 +213,8 @@ def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, sca
     if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_tables must be [B][W] and seq_lens [B]")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    workspace = _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, q.device, stream)
     st = lib().paged_decode_attn(
         _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
         _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
@@ -216,9 +238,8 @@ def paged_decode_attn_masked(q, k_pool, v_pool, block_tables, seq_lens, block_si
     if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_tables must be [B][W] and seq_lens [B]")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    workspace = _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, q.device, stream)
     st = lib().paged_decode_attn_masked(
         _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
         _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
@@ -243,9 +264,8 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables, seq_
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
         raise ValueError("k_new / v_new must be [B][Hkv][D]")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    workspace = _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, q.device, stream)
     st = lib().paged_decode_attn_append(
         _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
         _dev(k_new, "k_new", torch.float16, 3), _dev(v_new, "v_new", torch.float16, 3),
@@ -307,9 +327,9 @@ def paged_gather_kv(k_pool, v_pool, block_tables, seq_lens, block_size, k_out=No
     B, W = block_tables.shape
     shape = (B, Hkv, W * block_size, D)
     if k_out is None:
-        k_out = torch.zeros(shape, dtype=torch.float16, device=k_pool.device)
+        k_out = _new_on(stream, shape, torch.float16, k_pool.device, zero=True)
     if v_out is None:
-        v_out = torch.zeros(shape, dtype=torch.float16, device=k_pool.device)
+        v_out = _new_on(stream, shape, torch.float16, k_pool.device, zero=True)
     st = lib().paged_gather_kv(
         _dev(k_out, "k_out", torch.float16, 4), _dev(v_out, "v_out", torch.float16, 4),
         _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
@@ -370,9 +390,8 @@ def paged_decode_attn_fp8(q, k_pool, v_pool, block_tables, seq_lens, block_size,
     if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_tables must be [B][W] and seq_lens [B]")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    workspace = _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, q.device, stream)
     st = lib().paged_decode_attn_fp8(
         _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
         _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
@@ -398,9 +417,8 @@ def paged_decode_attn_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables, 
     if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_tables must be [B][W] and seq_lens [B]")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(B, Hq, Hkv, D, block_size, W, device=q.device)
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    workspace = _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, q.device, stream)
     st = lib().paged_decode_attn_append_fp8(
         _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
         _dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),

@@ -49,6 +49,19 @@ def test_every_declared_symbol_is_exported(pa):
         assert re.search(rf"\bT {n}$", out, re.M), n
 
 
+def test_binding_defines_every_call(pa):
+    # the Python binding has a function for every C entry point (same name;
+    # pa_probe_read is bound as probe_read), plus the workspace helper
+    import inspect
+
+    for n in declared_functions():
+        name = "probe_read" if n == "pa_probe_read" else n
+        if n == "pa_status_string":
+            continue
+        assert inspect.isfunction(getattr(pa, name, None)), name
+    assert inspect.isfunction(getattr(pa, "new_workspace", None))
+
+
 def test_status_strings(pa):
     L = pa.lib()
     for s, word in [(0, b"PA_OK"), (1, b"INVALID_ARG"), (2, b"UNSUPPORTED"), (3, b"HIP"), (4, b"WORKSPACE")]:
