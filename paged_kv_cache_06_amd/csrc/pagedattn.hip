@@ -21,6 +21,8 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -91,27 +93,21 @@ int cu_count() {
     return n;
 }
 
-// Resident workgroups per compute unit for a decode kernel (cached per
-// device and kernel; the kernel set is small and fixed).
+// Resident workgroups per compute unit for a decode kernel, cached per
+// (kernel, device) under a lock: the query is made once, and a reader never
+// sees one kernel's entry with another's count.
 int blocks_per_cu(const DecodeFn& f) {
-    struct Entry {
-        std::atomic<const void*> fn;
-        std::atomic<int> dev, occ;
-    };
-    static Entry cache[256];
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const size_t h = (reinterpret_cast<uintptr_t>(f.fn) / 16 + (size_t)dev * 31) % 256;
-    Entry& e = cache[h];
-    if (e.fn.load(std::memory_order_acquire) == f.fn && e.dev.load(std::memory_order_relaxed) == dev) {
-        const int o = e.occ.load(std::memory_order_relaxed);
-        if (o > 0) return o;
-    }
+    const std::pair<const void*, int> key{f.fn, dev};
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f.fn, f.threads, 0) != hipSuccess || occ <= 0) occ = 1;
-    e.occ.store(occ, std::memory_order_relaxed);
-    e.dev.store(dev, std::memory_order_relaxed);
-    e.fn.store(f.fn, std::memory_order_release);
+    cache.emplace(key, occ);
     return occ;
 }
 
