@@ -110,15 +110,19 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
                     void *stream);
 
 /*
- * Bytes of device workspace paged_decode_attn needs for these sizes: the
+ * Bytes of device workspace paged_decode_attn needs for these sizes: a fixed
+ * region of 32 KiB at the start holding the int32 arrival counters of the
+ * split-sequence reduction (one per (row, KV head) of a launch), then the
  * fp32 partial results (max, sum, unnormalised output per query head) of up
- * to P = min(64, T) sequence partitions per (row, KV head), T =
- * ceil(W*block_size/64) being the number of 64-token tiles of a full row,
- * rounded up to 256 bytes, then the per-(row, KV head) int32 arrival counters
- * of the split-sequence reduction, rounded up to 256 bytes. The value never
- * decreases when any argument grows. The same size serves the E4M3-pool
- * calls (their 128-token tiles give at most as many partitions).
- * Returns 0 for invalid sizes.
+ * to P = min(64, T) sequence partitions per (row, KV head) of min(num_seqs,
+ * 512) rows, T = ceil(W*block_size/64) being the number of 64-token tiles
+ * of a full row, rounded up to 256 bytes. A launch covers
+ * min(num_seqs, 512, 8192 / num_kv_heads) rows; larger batches run as
+ * several launches in order on the stream, which reuse the same counters
+ * and partials. The value never decreases when any argument grows. The same
+ * size serves the E4M3-pool calls (their 128-token tiles give at most as
+ * many partitions). Returns 0 for invalid sizes (num_kv_heads > 8192
+ * included).
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block_size, int32_t max_blocks_per_seq);
@@ -126,11 +130,11 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
 /*
  * Zero a workspace with a device fill kernel (no memset, so it may be
  * captured in a HIP graph). A workspace must be all-zero before its first
- * paged_decode_attn call. The partials sit at its start and the counters at
- * its end, and every completed call leaves its counters at zero again, so
- * one init per allocation suffices for any sequence of calls whose sizes the
- * workspace covers (e.g. sized with the largest num_seqs and
- * max_blocks_per_seq used).
+ * paged_decode_attn call. The counters sit in a region of fixed size at its
+ * start that no partial result ever overlaps, and every completed call
+ * leaves its counters at zero again, so one init per allocation suffices
+ * for any sequence of calls whose workspace size the allocation covers
+ * (e.g. sized with the largest num_seqs and max_blocks_per_seq used).
  */
 pa_status paged_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

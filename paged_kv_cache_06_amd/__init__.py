@@ -10,6 +10,9 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
   kv_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, block_size)
   paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size,
                     scale, out=None, workspace=None)
+      (workspace=None: a zeroed workspace kept by the binding per (device,
+      stream) and reused by later calls on that stream; calls to be
+      captured in a HIP graph should pass their own, made beforehand)
   paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables,
                            seq_lens, block_size, scale, out=None,
                            workspace=None)   (the two calls above, fused)
@@ -194,12 +197,30 @@ def _new_on(stream, shape, dtype, device, zero=False):
         return (torch.zeros if zero else torch.empty)(shape, dtype=dtype, device=device)
 
 
+# Workspaces the binding keeps for calls made without one: one per (device,
+# stream), grown (never shrunk) to the largest size asked for on that stream.
+# Calls on one stream run in order, and each leaves the workspace's counters
+# at zero, so they can share it; calls on different streams get different
+# ones. A replacement is made on the same stream, so torch's allocator does
+# not hand the old memory out again while queued calls may still use it.
+_ws_cache = {}
+
+
 def _call_workspace(workspace, B, Hq, Hkv, D, block_size, W, device, stream):
-    """The caller's workspace, or a zeroed temporary one made on the call's stream."""
+    """The caller's workspace, or the binding's cached one for the call's
+    (device, stream), zero-filled on that stream when it is made."""
     if workspace is not None:
         return workspace
-    with _on(stream):
-        return new_workspace(B, Hq, Hkv, D, block_size, W, device=device)
+    n = paged_decode_workspace_size(B, Hq, Hkv, D, block_size, W)
+    dev = torch.device(device)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), s.cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < n:
+        with torch.cuda.stream(s):
+            ws = new_workspace(B, Hq, Hkv, D, block_size, W, device=dev)
+        _ws_cache[key] = ws
+    return ws
 
 
 def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, out=None, workspace=None,

@@ -60,10 +60,16 @@ struct Plan {
     int P;             // partials per (row, KV head), at most
 };
 
+// Arrival counters: a fixed region at the start of the workspace, one int32
+// per (row, KV head) of a launch. Launches of one call run in order on one
+// stream and each leaves its counters at zero, so they share the region.
+constexpr int kCounterSlots = 8192;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+
 Plan make_plan(int B, int Hkv, int bs, int W, int tt) {
     Plan pl;
     pl.wtiles = ((long long)W * bs + tt - 1) / tt;
-    pl.rows = std::max(1, std::min(B, kMaxRows));
+    pl.rows = std::max(1, std::min({B, kMaxRows, kCounterSlots / Hkv}));
     pl.P = (int)std::min<long long>(kMaxParts, pl.wtiles);
     // a (row, KV head) of nt tiles meets at most 1 + ceil((nt-1)/C) ranges of >= C tiles
     pl.C = pl.P > 1 ? (int)((pl.wtiles - 1 + pl.P - 2) / (pl.P - 1)) : 1;
@@ -71,13 +77,14 @@ Plan make_plan(int B, int Hkv, int bs, int W, int tt) {
 }
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
-size_t counters_bytes(int B, int Hkv) { return round256((size_t)B * Hkv * 4); }
 size_t partials_bytes(int B, int Hq, int D, int P) { return round256((size_t)B * P * Hq * (D + 2) * 4); }
 
-// Workspace layout: the partials from the start, the arrival counters at the
-// (256-byte aligned) end. Every call leaves its counters at zero, so a
-// workspace sized for a shape that bounds every call made with it serves all
-// of them: no call's partials reach into any call's counters.
+// Workspace layout: the arrival counters in a fixed region at the start
+// (kCounterBytes), then the fp32 partials of one launch's rows: (max, sum)
+// per query head of every partition, then the unnormalised outputs. The
+// counter region does not depend on the call's sizes, so no call's partials
+// ever reach any call's counters, and a workspace sized for a shape serves
+// every call whose partials fit in it.
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -133,12 +140,13 @@ int paged_decode_supported(int32_t num_heads, int32_t num_kv_heads, int32_t head
 
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block_size, int32_t max_blocks_per_seq) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
-        block_size <= 0 || max_blocks_per_seq <= 0)
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > kCounterSlots ||
+        num_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
         return 0;
-    const size_t rows = (size_t)(num_seqs > 0 ? num_seqs : 1);
-    const Plan pl = make_plan((int)rows, num_kv_heads, block_size, max_blocks_per_seq, tile_tokens(false));
-    return partials_bytes((int)rows, num_heads, head_dim, pl.P) + counters_bytes((int)rows, num_kv_heads);
+    const Plan pl = make_plan(std::max(num_seqs, 1), num_kv_heads, block_size, max_blocks_per_seq, tile_tokens(false));
+    // partials for min(B, kMaxRows) rows, a bound on a launch's rows that does not
+    // depend on num_kv_heads, so that the size never shrinks when an argument grows
+    return kCounterBytes + partials_bytes(std::min(std::max(num_seqs, 1), kMaxRows), num_heads, head_dim, pl.P);
 }
 
 pa_status paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -169,8 +177,9 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* workspace,
                         size_t workspace_bytes, void* stream, int32_t width = 0, PoolFormat fmt = kFp16Pool) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
-        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !std::isfinite(scale))
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > kCounterSlots ||
+        num_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+        !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
     auto scale_ok = [&](float x) { return std::isfinite(x) && (fmt.fp8 ? x >= 0x1p-96f && x <= 0x1p96f : x > 0.f); };
     if (!scale_ok(fmt.k_scale) || !scale_ok(fmt.v_scale)) return PA_ERR_INVALID_ARG;
@@ -191,14 +200,16 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
     const Plan pl = make_plan(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, tile_tokens(fmt.fp8));
     const int slots = blocks_per_cu(fn) * cu_count();
     char* ws = static_cast<char*>(workspace);
-    int32_t* counters = reinterpret_cast<int32_t*>(ws + (workspace_bytes / 256 * 256 - counters_bytes(num_seqs, num_kv_heads)));
-    float* part_ml = reinterpret_cast<float*>(ws);
-    float* part_acc = part_ml + (size_t)num_seqs * pl.P * num_heads * 2;
+    int32_t* counters = reinterpret_cast<int32_t*>(ws);
+    float* part_ml = reinterpret_cast<float*>(ws + kCounterBytes);
+    float* part_acc = part_ml + (size_t)pl.rows * pl.P * num_heads * 2;
     float sl2 = scale * fmt.k_scale * 1.4426950408889634f;
     float ksc = fmt.k_scale, vsc = fmt.v_scale, kinv = 1.0f / fmt.k_scale, vinv = 1.0f / fmt.v_scale;
     int Hkv = num_kv_heads, W = max_blocks_per_seq, N = num_blocks, C = pl.C, P = pl.P;
-    // Rows are processed kMaxRows at a time (the workgroups keep the rows'
-    // lengths in LDS); each launch covers its own rows of every buffer.
+    // Rows are processed pl.rows at a time (the workgroups keep the rows'
+    // lengths in LDS); each launch covers its own rows of q, out, the tables
+    // and the new tokens, and reuses the counters and partials of the one
+    // before it, which it follows on the stream.
     for (int r0 = 0; r0 < num_seqs; r0 += pl.rows) {
         int Bc = std::min(pl.rows, num_seqs - r0);
         const long long grid = std::min<long long>(slots, (long long)Bc * Hkv * pl.wtiles);
@@ -208,9 +219,9 @@ pa_status launch_decode(uint16_t* out, const uint16_t* q, void* k_pool, void* v_
         const int32_t* ll = seq_lens + r0;
         const uint16_t* kn = k_new ? k_new + (size_t)r0 * num_kv_heads * head_dim : nullptr;
         const uint16_t* vn = v_new ? v_new + (size_t)r0 * num_kv_heads * head_dim : nullptr;
-        int32_t* cc = counters + (size_t)r0 * Hkv;
-        float* pm = part_ml + (size_t)r0 * P * num_heads * 2;
-        float* pa = part_acc + (size_t)r0 * P * num_heads * head_dim;
+        int32_t* cc = counters;
+        float* pm = part_ml;
+        float* pa = part_acc;
         void* args[] = {&o, (void*)&qq, (void*)&k_pool, (void*)&v_pool, (void*)&tt, (void*)&ll, (void*)&kn,
                         (void*)&vn, &cc, &pm, &pa, &Bc, &Hkv, &W, &N, &C, &P, &sl2, &width, &ksc, &vsc, &kinv, &vinv};
         if (hipLaunchKernel(fn.fn, dim3((unsigned)grid), dim3(fn.threads), args, 0, (hipStream_t)stream) !=

@@ -82,17 +82,29 @@ def test_supported_shapes(pa):
 
 
 def test_workspace_size_arithmetic(pa):
-    # B * partitions * Hq * (D+2) fp32 + counters (B*Hkv int32), each rounded to 256 B,
-    # partitions = min(64, tiles), tiles = ceil(W*bs/64)
+    # a fixed 32 KiB counter region, then B' * partitions * Hq * (D+2) fp32 rounded to 256 B, where
+    # B' = min(B, 512) rows (a bound on one launch's rows) and partitions = min(64, tiles), tiles = ceil(W*bs/64)
     def expect(B, Hq, Hkv, D, bs, W):
         tiles = -(-W * bs // 64)
         parts = min(64, tiles)
-        return -(-(B * Hkv * 4) // 256) * 256 + -(-(B * parts * Hq * (D + 2) * 4) // 256) * 256
+        rows = max(1, min(B, 512))
+        return 32768 + -(-(rows * parts * Hq * (D + 2) * 4) // 256) * 256
 
     for args in [(32, 12, 2, 128, 64, 68), (95, 12, 2, 128, 16, 144), (4, 2, 1, 64, 16, 5), (1, 8, 8, 64, 128, 3),
-                 (2, 12, 2, 128, 64, 400), (1000, 12, 2, 128, 16, 300)]:
+                 (2, 12, 2, 128, 64, 400), (1000, 12, 2, 128, 16, 300), (600, 64, 32, 64, 16, 8)]:
         assert pa.paged_decode_workspace_size(*args) == expect(*args)
     assert pa.paged_decode_workspace_size(4, 12, 5, 128, 64, 4) == 0
+    assert pa.paged_decode_workspace_size(4, 16384, 16384, 64, 16, 4) == 0  # more KV heads than counter slots
+
+
+def test_workspace_size_monotone(pa):
+    # a workspace sized for the larger of two shapes serves both: the size never shrinks as any argument grows
+    base = (32, 12, 2, 128, 64, 68)
+    n0 = pa.paged_decode_workspace_size(*base)
+    for i, grown in enumerate([(256, 12, 2, 128, 64, 68), (32, 24, 2, 128, 64, 68), (32, 12, 2, 256, 64, 68),
+                               (32, 12, 2, 128, 128, 68), (32, 12, 2, 128, 64, 300), (600, 12, 2, 128, 64, 68),
+                               (32, 12, 4, 128, 64, 68), (600, 64, 32, 64, 16, 68)]):
+        assert pa.paged_decode_workspace_size(*grown) >= n0, i
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every case returns before a launch

@@ -310,3 +310,27 @@ def test_unsupported_shape_raises(torch, pa):
     with pytest.raises(pa.PagedAttnError) as e:
         pa.paged_decode_attn(q, k, v, t, s, 8, 0.1)
     assert e.value.status == 2
+
+
+def test_workspace_sized_for_long_rows_serves_a_wider_batch(torch, pa, oracle):
+    # A workspace sized for 32 rows of a 300-block table (bs 64) also covers a
+    # 256-row batch of 4-block tables by size. The counters sit in a region
+    # of their own, so the first call's partials cannot land on the second
+    # call's counters: both calls, and the first one again, match the oracle.
+    ws = pa.new_workspace(32, 12, 2, 128, 64, 300)
+    assert pa.paged_decode_workspace_size(256, 12, 2, 128, 64, 4) <= ws.numel()
+    rng = np.random.default_rng(31)
+    long_lens = [int(x) for x in rng.integers(8000, 19200, size=32)]
+    wa = wl.make_workload("long32", 32, 12, 2, 128, 64, sum(wl.blocks_for(L, 64) for L in long_lens) + 8,
+                          long_lens, seed=32, events=10)
+    wide_lens = [int(x) for x in rng.integers(1, 257, size=256)]
+    wb = wl.make_workload("wide256", 256, 12, 2, 128, 64, sum(wl.blocks_for(L, 64) for L in wide_lens) + 8,
+                          wide_lens, seed=33, events=10)
+    assert wa.W >= 126 and wb.W <= 4
+    for name, w in [("long rows", wa), ("wide batch", wb), ("long rows again", wa)]:
+        ld = w.layer(0)
+        say("workspace reuse", name)
+        out = host(run_decode(torch, pa, w, upload(torch, w, ld), ws=ws))
+        ref, _ = oracle.paged_decode_attn(ld.q, ld.k_pool, ld.v_pool, w.tables, w.seq_lens, w.bs, w.scale,
+                                          nthreads=NTHREADS)
+        assert_close(out, ref, f"workspace reuse: {name}")
