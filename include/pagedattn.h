@@ -76,7 +76,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, misalignment */
     PA_ERR_UNSUPPORTED = 2, /* (block_size, head_dim, Hq/Hkv) combination not compiled in */
     PA_ERR_HIP = 3,         /* the kernel launch failed */
-    PA_ERR_WORKSPACE = 4    /* workspace null or smaller than paged_decode_workspace_size() */
+    PA_ERR_WORKSPACE = 4,   /* workspace null or smaller than paged_decode_workspace_size() */
+    PA_ERR_SCRATCH = 5      /* paged_decode_attn_noalloc: the call needs more than its 32 MiB scratch */
 } pa_status;
 
 /* Static string naming a status. Never NULL. */
@@ -165,6 +166,30 @@ pa_status paged_decode_attn(uint16_t *out, const uint16_t *q, const uint16_t *k_
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * paged_decode_attn_noalloc -- paged_decode_attn for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * conventions, results (bit-identical, same kernel) and errors as
+ * paged_decode_attn, without the workspace arguments: the workspace is a
+ * static device array inside the library, 32 MiB per GPU, held by every GPU
+ * the library runs on until the process ends. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); it only enqueues
+ * the decode on `stream`, and on its first call on a device also a small
+ * zero fill of the array's counter region ahead of it.
+ * Limit: calls whose paged_decode_workspace_size() exceeds 32 MiB return
+ * PA_ERR_SCRATCH before anything is enqueued (e.g. 32 rows of 12/2/128 heads
+ * with tables of up to 300 blocks of 64 tokens need 12.8 MiB).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: two calls in flight at the same time on one GPU (different
+ * streams, or a graph replayed concurrently with a direct call) race on it
+ * and give unspecified results. Calls in order on one stream are safe.
+ */
+pa_status paged_decode_attn_noalloc(uint16_t *out, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void *stream);
 
 /*
  * paged_decode_attn_append -- kv_append followed by paged_decode_attn, in one

@@ -13,6 +13,9 @@ Names and argument order follow the C ABI in ``include/pagedattn.h``:
       (workspace=None: a zeroed workspace kept by the binding per (device,
       stream) and reused by later calls on that stream; calls to be
       captured in a HIP graph should pass their own, made beforehand)
+  paged_decode_attn_noalloc(q, k_pool, v_pool, block_tables, seq_lens,
+                            block_size, scale, out=None)   (no workspace:
+                                                           static scratch)
   paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, block_tables,
                            seq_lens, block_size, scale, out=None,
                            workspace=None)   (the two calls above, fused)
@@ -51,7 +54,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
-_ERRORS = {1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_HIP", 4: "PA_ERR_WORKSPACE"}
+_ERRORS = {1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_HIP", 4: "PA_ERR_WORKSPACE",
+           5: "PA_ERR_SCRATCH"}
 
 _lib = None
 
@@ -83,6 +87,8 @@ def lib():
     L.paged_decode_workspace_init.restype = ctypes.c_int
     L.paged_decode_attn.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
     L.paged_decode_attn.restype = ctypes.c_int
+    L.paged_decode_attn_noalloc.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, vp]
+    L.paged_decode_attn_noalloc.restype = ctypes.c_int
     L.paged_decode_attn_append.argtypes = [vp] * 8 + [i32] * 7 + [ctypes.c_float, vp, sz, vp]
     L.paged_decode_attn_masked.argtypes = [vp] * 6 + [i32] * 7 + [ctypes.c_float, i32, vp, sz, vp]
     L.paged_decode_attn_masked.restype = ctypes.c_int
@@ -244,6 +250,29 @@ def paged_decode_attn(q, k_pool, v_pool, block_tables, seq_lens, block_size, sca
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream),
     )
     _check(st, "paged_decode_attn")
+    return out
+
+
+def paged_decode_attn_noalloc(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale, out=None, stream=None):
+    """paged_decode_attn with the library's static device scratch as its
+    workspace: the C call allocates nothing (pass `out` to allocate nothing
+    here either). Calls that overlap on one GPU race on the scratch."""
+    N, Hkv, D = _pool_dims(k_pool, v_pool, block_size)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match the pools")
+    W = block_tables.shape[1]
+    if block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    if out is None:
+        out = _new_on(stream, (B, Hq, D), torch.float16, q.device)
+    st = lib().paged_decode_attn_noalloc(
+        _dev(out, "out", torch.float16, 3), _dev(q, "q", torch.float16, 3),
+        _dev(k_pool, "k_pool", torch.float16), _dev(v_pool, "v_pool", torch.float16),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, Hq, Hkv, D, block_size, W, N, ctypes.c_float(scale), _stream(stream),
+    )
+    _check(st, "paged_decode_attn_noalloc")
     return out
 
 

@@ -118,6 +118,39 @@ int blocks_per_cu(const DecodeFn& f) {
     return occ;
 }
 
+// Scratch of paged_decode_attn_noalloc: the decode's workspace (arrival
+// counters, then partials) in a static device array, so that the call
+// allocates nothing. Every GPU the library runs on holds its own copy for
+// the life of the process. In host code `scratch` only names the symbol: its
+// device address on the current GPU comes from hipGetSymbolAddress, kept per
+// device, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, guarded by g_scratch_mu
+
+// The current device's scratch address. On the first call on a device its
+// counter region is zero-filled by a kernel on `stream`, ahead of the
+// caller's launch on the same stream; every later call finds the counters
+// at zero, since each decode leaves them so.
+pa_status scratch_for_current_device(void** ptr, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PA_ERR_HIP;
+        const size_t words = kCounterBytes / 4;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(p), words);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +162,9 @@ const char* pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: block_size/head_dim/group size not compiled in";
         case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+        case PA_ERR_SCRATCH:
+            return "PA_ERR_SCRATCH: the call needs more workspace than the 32 MiB static scratch of "
+                   "paged_decode_attn_noalloc holds";
         default: return "unknown pa_status";
     }
 }
@@ -244,6 +280,22 @@ pa_status paged_decode_attn(uint16_t* out, const uint16_t* q, const uint16_t* k_
     return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
                          seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, scale, workspace, workspace_bytes, stream);
+}
+
+pa_status paged_decode_attn_noalloc(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t num_blocks, float scale, void* stream) {
+    const size_t need = paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                    max_blocks_per_seq);
+    if (need == 0) return PA_ERR_INVALID_ARG;
+    if (need > kScratchBytes) return PA_ERR_SCRATCH;
+    void* ws = nullptr;
+    const pa_status st = scratch_for_current_device(&ws, (hipStream_t)stream);
+    if (st != PA_OK) return st;
+    return launch_decode(out, q, const_cast<uint16_t*>(k_pool), const_cast<uint16_t*>(v_pool), block_tables,
+                         seq_lens, nullptr, nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, scale, ws, kScratchBytes, stream);
 }
 
 pa_status paged_decode_attn_masked(uint16_t* out, const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
               "paged_decode_workspace_init", "kv_copy_blocks", "kv_scatter_prefill", "paged_gather_kv",
               "pa_status_string", "kv_append_fp8", "paged_decode_attn_fp8", "paged_decode_attn_append_fp8",
               "kv_copy_blocks_fp8", "kv_scatter_prefill_fp8", "pa_probe_read",
-              "paged_decode_supported"]:
+              "paged_decode_supported", "paged_decode_attn_noalloc"]:
         assert n in names
 
 
@@ -64,7 +64,8 @@ def test_binding_defines_every_call(pa):
 
 def test_status_strings(pa):
     L = pa.lib()
-    for s, word in [(0, b"PA_OK"), (1, b"INVALID_ARG"), (2, b"UNSUPPORTED"), (3, b"HIP"), (4, b"WORKSPACE")]:
+    for s, word in [(0, b"PA_OK"), (1, b"INVALID_ARG"), (2, b"UNSUPPORTED"), (3, b"HIP"), (4, b"WORKSPACE"),
+                    (5, b"SCRATCH")]:
         assert word in L.pa_status_string(s)
     assert L.pa_status_string(99)
 
@@ -132,6 +133,24 @@ def test_decode_rejects_bad_arguments_on_host(pa):
     assert _decode(L, ws=None) == 4
     assert _decode(L, ws=ctypes.c_void_p((1 << 20) + 64)) == 4  # workspace must be 256-byte aligned
     assert _decode(L, B=0) == 0  # nothing to do
+
+
+def test_noalloc_rejects_oversized_and_invalid_calls_on_host(pa):
+    # Sizes are checked before the scratch is looked up or anything is enqueued
+    # (so no GPU is touched here): shapes whose workspace exceeds the 32 MiB
+    # scratch get PA_ERR_SCRATCH, invalid shapes PA_ERR_INVALID_ARG.
+    L = pa.lib()
+
+    def call(B=4, Hq=12, Hkv=2, D=128, bs=64, W=4):
+        return L.paged_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, Hq, Hkv, D, bs, W, 16,
+                                           ctypes.c_float(0.1), None)
+
+    big = (512, 64, 8, 128, 64, 4096)
+    assert pa.paged_decode_workspace_size(*big) > 32 << 20
+    assert call(*big) == 5
+    assert pa.paged_decode_workspace_size(32, 12, 2, 128, 64, 300) <= 32 << 20
+    assert call(Hq=12, Hkv=5) == 1
+    assert call(D=0) == 1
 
 
 def _decode_append(L, **kw):
