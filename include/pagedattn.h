@@ -116,9 +116,9 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
  * split-sequence reduction (one per (row, KV head) of a launch), then the
  * fp32 partial results (max, sum, unnormalised output per query head) of up
  * to P = min(64, T) sequence partitions per (row, KV head) of min(num_seqs,
- * 512) rows, T = ceil(W*block_size/64) being the number of 64-token tiles
+ * 256) rows, T = ceil(W*block_size/64) being the number of 64-token tiles
  * of a full row, rounded up to 256 bytes. A launch covers
- * min(num_seqs, 512, 8192 / num_kv_heads) rows; larger batches run as
+ * min(num_seqs, 256, 8192 / num_kv_heads) rows; larger batches run as
  * several launches in order on the stream, which reuse the same counters
  * and partials. The value never decreases when any argument grows. The same
  * size serves the E4M3-pool calls (their 128-token tiles give at most as

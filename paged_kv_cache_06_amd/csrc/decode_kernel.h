@@ -329,7 +329,7 @@ __device__ __forceinline__ int clamp_block(int blk, int N) {
 // decode kernel
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxRows = 512;    // rows per launch (longer batches are split by the host)
+constexpr int kMaxRows = 256;    // rows per launch (longer batches are split by the host)
 constexpr int kMaxParts = 64;    // partitions per (row, KV head)
 constexpr int kMaxPending = 4;   // split runs one workgroup may finish (at most its first and last)
 constexpr int kLenMask = 0x3fffffff;     // row length held in LDS ...
@@ -761,9 +761,13 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 rescale |= alpha[h] != 1.0f;
                 m[h] = mn;
                 float ps = 0.f;
+                // p enters PV and the sum as 2^15 * exp2(s - max) in fp16: the factor cancels in
+                // their ratio, and fp16 keeps its full 11-bit precision for scores down to 29
+                // (log2 units) below the running max instead of 14, subnormal p down to 39
+                const float mp = mref - 15.f;
 #pragma unroll
                 for (int hf = 0; hf < HALVES; ++hf) {
-                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[hf][h] - mref);
+                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[hf][h] - mp);
                     ps += (float)ph;
                     s_p[wip][h][64 * hf + lane] = ph;
                 }

@@ -386,3 +386,38 @@ CONFIGS = {
     "high_occupancy": high_occupancy,
     "full_step": full_step,
 }
+
+
+def dominant_key(bands, L=16384, seed=41, Hq=12, Hkv=2, D=128, bs=64) -> Workload:
+    """Rows whose scores have one dominant key and a long tail a set gap
+    below it: row i has length L (the last row L//4 + 1, a ragged length),
+    query heads all (a, 0, ..., 0), and K channel 0 chosen so that
+    scale * q . k_t = s_top - gap_t, the gaps drawn uniformly from
+    bands[i] = (lo, hi) in natural-log units, the dominant key at a seeded
+    position. Other K channels, V, and stale slots are N(0,1)."""
+    B = len(bands)
+    lens = [L] * (B - 1) + [L // 4 + 1]
+    N = sum(blocks_for(n, bs) for n in lens) + 4
+    w = make_workload("dominant_key", B, Hq, Hkv, D, bs, N, lens, seed, events=10)
+    base = w._layer_fn
+    a = np.float16(8.0)  # query channel 0
+    unit = float(np.float32(w.scale)) * float(a)  # score per unit of K channel 0
+    s_top = 32.0
+
+    def fn(layer: int) -> LayerData:
+        ld = base(layer)
+        rng = np.random.default_rng(seed + 7 + 1000 * layer)
+        ld.q[:] = 0
+        ld.q[:, :, 0] = a
+        for b, (lo, hi) in enumerate(bands):
+            n = int(lens[b])
+            k_log, v_log = read_row(ld.k_pool, ld.v_pool, w.tables[b], n, bs)
+            gaps = rng.uniform(lo, hi, size=(n, Hkv))
+            gaps[int(rng.integers(0, n))] = 0.0
+            k_log[:, :, 0] = ((s_top - gaps) / unit).astype(np.float16)
+            write_row(ld.k_pool, ld.v_pool, w.tables[b], k_log, v_log, bs)
+        return ld
+
+    w._layer_fn = fn
+    w.name = "dominant_key"
+    return w
