@@ -32,6 +32,16 @@ same two measurements), the ceiling any kernel reading those bytes meets at
 that size. `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload, on the host's threads and on one thread.
 
+`graded` (default run only) times the same step on the three workloads
+the 70 %-of-peak target is set on -- the mixed batch (31 rows of 16..512
+tokens and one of 4,352), uniform batch 32 at 4,096 tokens, and the 28-layer
+step -- with `--graded-steps` timed steps each, and reports for each the
+decode kernel's duration (the same smaller-of-two upper bounds), its GB/s
+and fraction of 8 TB/s over the workload's unique algorithmic bytes, whether
+that meets 0.70 and the duration that would, the recorded HBM traffic where
+profiles/ holds it for the current kernel code, the same-size streaming
+read, and the whole step's rows*layers/s. `--no-graded` skips it.
+
 Other modes (`--op`): fp8 (the step over E4M3 pools), contrast (the mixed
 batch paged, contiguous, at masked full width and at block sizes 16..256),
 copy_blocks (copy-on-write block copies), scatter_prefill (the post-prefill
@@ -641,70 +651,10 @@ def bench_contrast(args, torch, pa):
     print(json.dumps(line), flush=True)
 
 
-def parse():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="uniform1024", choices=sorted(wl.CONFIGS))
-    ap.add_argument("--replicas", type=int, default=0, help="pool replicas rotated per step (0 = auto, ~1 GiB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed sample")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help=f"after the bench, run {COPY_REPS} plain device copies of MIB MiB (counter calibration)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
-    ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
-    ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
-    ap.add_argument("--pmc-fp8", action="store_true", help="--pmc-summary of an --op fp8 run (E4M3-pool kernel)")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast", "fp8"],
-                    help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
-                         "scatter_prefill: the post-prefill scatter alone; contrast: the mixed batch decoded "
-                         "paged, contiguous, at masked full width, and at block sizes 16..256; fp8: the step "
-                         "over E4M3 pools on --config's shapes")
-    ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
-    ap.add_argument("--kv", default="f16", choices=["f16", "fp8"], help="scatter_prefill: pool format")
-    return ap.parse_args()
-
-
-def main():
-    args = parse()
-    if args.pmc_summary:
-        text = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.pmc_copy_mib << 20,
-                           args.pmc_command, fp8=args.pmc_fp8)
-        os.makedirs(PROFILES, exist_ok=True)
-        with open(traffic_file(args.config, args.pmc_fp8), "w") as f:
-            f.write(text)
-        print(text, end="")
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(
-            f"bench.py measures one GPU only: the decode path has no cross-GPU step here "
-            f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
-            file=sys.stderr,
-        )
-        sys.exit(2)
-
-    import torch
-
-    import paged_kv_cache_06_amd as pa
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    if args.op == "copy_blocks":
-        bench_copy_blocks(args, torch, pa)
-        return
-    if args.op == "scatter_prefill":
-        bench_scatter_prefill(args, torch, pa)
-        return
-    if args.op == "contrast":
-        bench_contrast(args, torch, pa)
-        return
-    if args.op == "fp8":
-        bench_fp8(args, torch, pa)
-        return
-    w = wl.CONFIGS[args.config]()
+def measure(args, torch, pa, w, steps, warmup, with_cpu):
+    """Time the step on workload w: the fused step and the two-call step back to
+    back, a HIP graph replay, per-launch event brackets, a same-size streaming
+    read, and (with_cpu) the CPU oracle on a bounded sample."""
     layers = w.layers
 
     # ---- inputs, resident on the device
@@ -740,17 +690,17 @@ def main():
             pa.paged_decode_attn(q, kp, vp, tables, lens, w.bs, w.scale, out=out, workspace=ws)
 
     def time_steps(fn):
-        for i in range(args.warmup):
+        for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        for i in range(args.steps):
+        for i in range(steps):
             fn(i)
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps
+        return t0.elapsed_time(t1) / steps
 
     # ---- whole-step throughput (the two-call form of the same step beside it)
     ms_per_step = time_steps(step)
@@ -758,13 +708,13 @@ def main():
 
     # ---- the same steps replayed from a HIP graph: one capture of G = min(R, K)
     # consecutive steps (through G replicas), replayed until K steps have run
-    G = min(R, args.steps)
+    G = min(R, steps)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(G):
             step(i)
-    reps = max(1, math.ceil(args.steps / G))
-    for _ in range(max(1, math.ceil(args.warmup / G))):
+    reps = max(1, math.ceil(steps / G))
+    for _ in range(max(1, math.ceil(warmup / G))):
         graph.replay()
     torch.cuda.synchronize()
     g0 = torch.cuda.Event(enable_timing=True)
@@ -778,7 +728,7 @@ def main():
     del graph
 
     # ---- per-launch durations (events around each launch)
-    n_k = max(20, min(args.steps, 400))
+    n_k = max(20, min(steps, 400))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
     for i in range(n_k):
@@ -829,7 +779,7 @@ def main():
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         import oracle
 
         orc = oracle.get()
@@ -863,6 +813,124 @@ def main():
             "single_thread_sample": f"{reps1} x the same on 1 thread, {t_used1:.2f} s",
             "cpu_model": cpu_model(),
         }
+
+    return dict(w=w, layers=layers, R=R, ms_per_step=ms_per_step, two_call_ms_per_step=two_call_ms_per_step,
+                graph_ms_per_step=graph_ms_per_step, dec_kernel_ms=dec_kernel_ms, dec_b2b_ms=dec_b2b_ms,
+                dec_graph_ms=dec_graph_ms, dec_ms=dec_ms, dec_only_b2b_ms=dec_only_b2b_ms, app_ms=app_ms,
+                probe_us=probe_us, probe_bytes=probe_bytes, launch_bytes=launch_bytes,
+                unique_launch_bytes=unique_launch_bytes, step_bytes=step_bytes, unique_step_bytes=unique_step_bytes,
+                value=value, dec_gbs=dec_gbs, dec_unique_gbs=dec_unique_gbs, cpu=cpu)
+
+
+GRADED = ("mixed", "uniform4096", "full_step")
+TARGET_FRAC = 0.70
+
+
+def graded_entry(m):
+    """The decode kernel on one workload against the 70 %-of-peak target."""
+    w = m["w"]
+    frac = m["dec_unique_gbs"] / PEAK_HBM_GBS
+    return {
+        "decode_us": round(m["dec_kernel_ms"] * 1e3, 3),
+        "GBs": round(m["dec_unique_gbs"], 2),
+        "frac": round(frac, 4),
+        "meets_target": bool(frac >= TARGET_FRAC),
+        "target_decode_us": round(m["unique_launch_bytes"] / (TARGET_FRAC * PEAK_HBM_GBS * 1e9) * 1e6, 3),
+        "bytes_per_launch": m["unique_launch_bytes"],
+        "traffic": read_traffic(w.name),
+        "probe_read_us": round(m["probe_us"], 3),
+        "decode_over_probe_time": round(m["dec_kernel_ms"] * 1e3 / m["probe_us"], 3),
+        "ms_per_step": round(m["ms_per_step"], 6),
+        "rows_layers_per_s": round(w.B * m["layers"] / (m["ms_per_step"] * 1e-3), 1),
+        "layers": m["layers"],
+        "seq_len_sum": int(w.seq_lens.sum()),
+    }
+
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="uniform1024", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--replicas", type=int, default=0, help="pool replicas rotated per step (0 = auto, ~1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help=f"after the bench, run {COPY_REPS} plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
+    ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
+    ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
+    ap.add_argument("--pmc-fp8", action="store_true", help="--pmc-summary of an --op fp8 run (E4M3-pool kernel)")
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast", "fp8"],
+                    help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
+                         "scatter_prefill: the post-prefill scatter alone; contrast: the mixed batch decoded "
+                         "paged, contiguous, at masked full width, and at block sizes 16..256; fp8: the step "
+                         "over E4M3 pools on --config's shapes")
+    ap.add_argument("--copy-pairs", type=int, default=1024, help="copy_blocks: block pairs per call")
+    ap.add_argument("--kv", default="f16", choices=["f16", "fp8"], help="scatter_prefill: pool format")
+    ap.add_argument("--no-graded", action="store_true",
+                    help="skip the mixed, uniform-4096 and 28-layer workloads timed beside the default one")
+    ap.add_argument("--graded-steps", type=int, default=40, help="timed steps of each graded workload")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        text = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.pmc_copy_mib << 20,
+                           args.pmc_command, fp8=args.pmc_fp8)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_file(args.config, args.pmc_fp8), "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            f"bench.py measures one GPU only: the decode path has no cross-GPU step here "
+            f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_06_amd as pa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, torch, pa)
+        return
+    if args.op == "scatter_prefill":
+        bench_scatter_prefill(args, torch, pa)
+        return
+    if args.op == "contrast":
+        bench_contrast(args, torch, pa)
+        return
+    if args.op == "fp8":
+        bench_fp8(args, torch, pa)
+        return
+    w = wl.CONFIGS[args.config]()
+    m = measure(args, torch, pa, w, args.steps, args.warmup, not args.no_cpu_baseline)
+    graded = None
+    if not args.no_graded and args.config == "uniform1024":
+        graded = {"target_frac": TARGET_FRAC}
+        for name in GRADED:
+            gm = measure(args, torch, pa, wl.CONFIGS[name](), args.graded_steps, min(args.warmup, 10), False)
+            graded[name] = graded_entry(gm)
+            del gm
+            torch.cuda.empty_cache()
+    layers, R = m["layers"], m["R"]
+    ms_per_step, two_call_ms_per_step = m["ms_per_step"], m["two_call_ms_per_step"]
+    graph_ms_per_step, dec_kernel_ms, dec_b2b_ms = m["graph_ms_per_step"], m["dec_kernel_ms"], m["dec_b2b_ms"]
+    dec_graph_ms, dec_ms, dec_only_b2b_ms, app_ms = m["dec_graph_ms"], m["dec_ms"], m["dec_only_b2b_ms"], m["app_ms"]
+    probe_us, probe_bytes, step_bytes = m["probe_us"], m["probe_bytes"], m["step_bytes"]
+    unique_step_bytes, unique_launch_bytes = m["unique_step_bytes"], m["unique_launch_bytes"]
+    value, dec_gbs, dec_unique_gbs, cpu = m["value"], m["dec_gbs"], m["dec_unique_gbs"], m["cpu"]
 
     cfg = {
         "workload": w.name,
@@ -922,6 +990,7 @@ def main():
                        "GBs": round(probe_bytes / (probe_us * 1e-6) / 1e9, 2),
                        "decode_over_probe_time": round(dec_kernel_ms * 1e3 / probe_us, 3)},
         "cpu_baseline": cpu,
+        "graded": graded,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
