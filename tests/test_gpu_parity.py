@@ -334,3 +334,38 @@ def test_workspace_sized_for_long_rows_serves_a_wider_batch(torch, pa, oracle):
         ref, _ = oracle.paged_decode_attn(ld.q, ld.k_pool, ld.v_pool, w.tables, w.seq_lens, w.bs, w.scale,
                                           nthreads=NTHREADS)
         assert_close(out, ref, f"workspace reuse: {name}")
+
+
+def test_one_workspace_for_relabelled_blocks_and_other_lengths(torch, pa, oracle):
+    # One workspace across calls of the same shapes: the mixed batch, the same
+    # lengths with every block relabelled (pools permuted to match), a
+    # different length mix, then the first call again. Every output matches
+    # the oracle, and the relabelled and repeated calls are bit-identical to
+    # the first.
+    wa = wl.CONFIGS["mixed"]()
+    lda = wa.layer(0)
+    perm = np.random.default_rng(61).permutation(wa.N).astype(np.int32)
+    tables_b = np.where(wa.tables >= 0, perm[np.maximum(wa.tables, 0)], -1).astype(np.int32)
+    kb = np.empty_like(lda.k_pool)
+    vb = np.empty_like(lda.v_pool)
+    kb[perm] = lda.k_pool
+    vb[perm] = lda.v_pool
+    wc = wl.make_workload("other_mix", wa.B, 12, 2, 128, 64, wa.N, np.roll(wa.seq_lens, 5), seed=62, events=30,
+                          W=wa.W)
+    ldc = wc.layer(0)
+    ws = pa.new_workspace(wa.B, 12, 2, 128, 64, wa.W)
+    cases = [("first", wa.tables, lda.q, lda.k_pool, lda.v_pool, wa.seq_lens),
+             ("relabelled", tables_b, lda.q, kb, vb, wa.seq_lens),
+             ("other lengths", wc.tables, ldc.q, ldc.k_pool, ldc.v_pool, wc.seq_lens),
+             ("first again", wa.tables, lda.q, lda.k_pool, lda.v_pool, wa.seq_lens)]
+    outs = {}
+    for name, tables, q, kp, vp, lens in cases:
+        say("workspace reuse:", name)
+        out = pa.paged_decode_attn(dev(torch, q), dev(torch, kp), dev(torch, vp), dev(torch, tables),
+                                   dev(torch, lens), 64, wa.scale, workspace=ws)
+        torch.cuda.synchronize()
+        outs[name] = host(out)
+        ref, _ = oracle.paged_decode_attn(q, kp, vp, tables, lens, 64, wa.scale, nthreads=NTHREADS)
+        assert_close(outs[name], ref, f"workspace reuse: {name}")
+    assert np.array_equal(outs["first"].view(np.uint16), outs["first again"].view(np.uint16))
+    assert np.array_equal(outs["first"].view(np.uint16), outs["relabelled"].view(np.uint16))
