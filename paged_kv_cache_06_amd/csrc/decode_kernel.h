@@ -17,17 +17,22 @@
 // the step's kv_append [SLM paged attention, "End-to-end flow"]. Pools hold
 // fp16 or E4M3 (FP8) elements (template argument F8); E4M3 tiles are widened
 // to fp16 in registers as they are used, exactly, and the pool's K and V
-// scales are folded into the score scale and the output. It runs on the
-// vector ALU (fp16 dot2 with fp32 accumulation): decode attention is a
-// matrix-vector product per KV group, bound by HBM bandwidth, so no matrix
-// cores. The design (persistent workgroups over balanced tile ranges, a load
-// wave issuing direct-to-LDS loads, compute waves per two query heads, the
-// merge by the last partition to arrive) is described above decode_kernel.
+// scales are folded into the score scale and the output.
+//
+// Both products of a tile run on the matrix cores (16x16x32 fp16, fp32
+// accumulate) with the group's query heads as the 16-wide side: scores as
+// K.Q^T, one 16-token block per product, and the output as V^T.P^T, 32
+// tokens per product. The kernel stays bound by HBM bandwidth; the matrix
+// cores take the instruction issue of the products off the vector ALU, so the
+// compute waves keep pace with the loads at a fraction of a tile's load time.
+// The design (persistent workgroups over balanced tile ranges, a load wave
+// issuing direct-to-LDS loads, two compute waves splitting each tile's tokens,
+// the merge by the last partition to arrive) is described above decode_kernel.
 //
 // Stale slots and unlisted blocks may hold NaN: scores of tokens past the
 // row's length are replaced (not multiplied) by -inf, and their V values are
-// zeroed before the dot products (fp16: in registers; E4M3: in LDS, by the
-// load wave).
+// zeroed before the products (fp16: in registers; E4M3: in LDS, by the load
+// wave, and in registers).
 
 #pragma once
 
@@ -61,27 +66,15 @@ using pa_detail::DecodeFn;
 
 // Tokens per tile: 64 for fp16 pools, 128 for E4M3 pools, so that a tile is
 // 16 KiB of K and 16 KiB of V at head_dim 128 in either format (the bytes a
-// workgroup keeps in flight set its share of the bandwidth). One lane per
-// token of each 64-token half in QK.
+// workgroup keeps in flight set its share of the bandwidth). The load wave
+// moves K one token per lane for each 64-token half of a tile.
 constexpr int tile_tokens(bool f8) { return f8 ? 128 : 64; }
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // wave-level helpers
 // ---------------------------------------------------------------------------
-
-// DPP controls (gfx9 encoding).
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kRowMirror = 0x140;   // lane i <-> 15-i within 16
-constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within 8
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
 
 // Combine lanes i and i^16, then i and i^32, with the gfx950 permlane swaps.
 template <class Op>
@@ -90,33 +83,6 @@ __device__ __forceinline__ float cross_rows(float x, Op op) {
     x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
     auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kQuadXor1>(x));
-    x = fmaxf(x, dpp<kQuadXor2>(x));
-    x = fmaxf(x, dpp<kHalfMirror>(x));
-    x = fmaxf(x, dpp<kRowMirror>(x));
-    return cross_rows(x, [](float a, float b) { return fmaxf(a, b); });
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp<kQuadXor1>(x);
-    x += dpp<kQuadXor2>(x);
-    x += dpp<kHalfMirror>(x);
-    x += dpp<kRowMirror>(x);
-    return cross_rows(x, [](float a, float b) { return a + b; });
-}
-
-__device__ __forceinline__ half2_t as_h2(unsigned int u) { return __builtin_bit_cast(half2_t, u); }
-
-// c + a.b over 8 fp16 pairs, fp32 accumulate (v_dot2_f32_f16).
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float c) {
-    c = __builtin_amdgcn_fdot2(as_h2(a.x), as_h2(b.x), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(b.y), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(b.z), c, false);
-    c = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(b.w), c, false);
-    return c;
 }
 
 // Two E4M3 bytes of w (bytes 0-1, or 2-3 with HI) as an fp16 pair, first
@@ -140,90 +106,27 @@ __device__ __forceinline__ u32x4 keep_first_bytes(int n) {
     };
     return u32x4{word(0), word(1), word(2), word(3)};
 }
-// Mask that keeps the first n (0..8 after clamping) fp16 values of a chunk of 8.
-__device__ __forceinline__ u32x4 keep_first(int n) {
-    u32x4 mask;
-    mask.x = (n > 0 ? 0xffffu : 0u) | (n > 1 ? 0xffff0000u : 0u);
-    mask.y = (n > 2 ? 0xffffu : 0u) | (n > 3 ? 0xffff0000u : 0u);
-    mask.z = (n > 4 ? 0xffffu : 0u) | (n > 5 ? 0xffff0000u : 0u);
-    mask.w = (n > 6 ? 0xffffu : 0u) | (n > 7 ? 0xffff0000u : 0u);
-    return mask;
-}
 
-// Scores of one 16-byte K chunk (channel pairs 4j..4j+3) against HPW query
-// heads: a[k][h] += q_h[pair 4j+k] . k[pair k], the query pair taken from
-// lane L0+k of this lane's 16-lane row by DPP row_newbcast. The compiler
-// cannot see inside the asm, so the block carries its own wait states: two
-// before it (a VALU result read by a DPP instruction) and three after it (a
-// dot result read by a different VALU instruction). Within a block every
-// accumulator is written once, so the dots need no spacing between them.
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][1], const unsigned (&q)[1], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %4, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[1][0]), "+v"(a[2][0]), "+v"(a[3][0])
-        : "v"(q[0]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
+// ---------------------------------------------------------------------------
+// matrix-core helpers
+// ---------------------------------------------------------------------------
+
+// v_mfma_f32_16x16x32_f16, C += A.B with A 16x32, B 32x16, fp32 accumulate.
+// Operands as 8 fp16 per lane: lane l holds A[l%16][8(l/16) .. 8(l/16)+7]
+// and B[8(l/16) .. 8(l/16)+7][l%16]; result element i of lane l is
+// C[4(l/16)+i][l%16].
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
 }
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][2], const unsigned (&q)[2], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %8, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %9, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %8, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %9, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %8, %12 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %9, %12 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %8, %13 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %9, %13 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[3][0]), "+v"(a[3][1])
-        : "v"(q[0]), "v"(q[1]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
+__device__ __forceinline__ unsigned pack_h2(_Float16 lo, _Float16 hi) {
+    return (unsigned)__builtin_bit_cast(uint16_t, lo) | ((unsigned)__builtin_bit_cast(uint16_t, hi) << 16);
 }
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][3], const unsigned (&q)[3], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %12, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %13, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %14, %15 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %12, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %13, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %14, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %12, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %13, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %8, %14, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %9, %12, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %10, %13, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %11, %14, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[2][2]), "+v"(a[3][0]), "+v"(a[3][1]), "+v"(a[3][2])
-        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
-}
-template <int L0>
-__device__ __forceinline__ void score_block(float (&a)[4][4], const unsigned (&q)[4], const u32x4& k) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %16, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %17, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %18, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %19, %20 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %4, %16, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %5, %17, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %6, %18, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %7, %19, %21 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %8, %16, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %9, %17, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %10, %18, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %11, %19, %22 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %12, %16, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %13, %17, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %14, %18, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %15, %19, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2\n\t"
-        : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[0][3]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[1][3]), "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[2][2]), "+v"(a[2][3]), "+v"(a[3][0]), "+v"(a[3][1]), "+v"(a[3][2]), "+v"(a[3][3])
-        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "n"(L0), "n"(L0 + 1), "n"(L0 + 2), "n"(L0 + 3));
+// Mask of the fp16 pair (first, first+1) of a run whose first n values are kept.
+__device__ __forceinline__ unsigned keep2(int n, int first) {
+    return (n > first ? 0xffffu : 0u) | (n > first + 1 ? 0xffff0000u : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -295,8 +198,8 @@ __device__ __forceinline__ void dma16(const void* src, unsigned dst) {
 }
 // Device-coherent (sc1) stores of the split-sequence partials and plain
 // stores of the output.
-__device__ __forceinline__ void st_f32_sc1(float* p, float v) {
-    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+__device__ __forceinline__ void st_f32x4_sc1(float* p, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void st_2f32_sc1(float* p, float a, float b) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -309,8 +212,12 @@ __device__ __forceinline__ void st_2f32_sc1(float* p, float a, float b) {
 constexpr int kCoherent = 16;                     // cache-policy bits: sc1
 constexpr int kRawBufferFormat = 0x00020000;      // dword3 of a raw 32-bit buffer resource
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ void st_b64(void* p, unsigned lo, unsigned hi) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v = {lo, hi};
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
 __device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
     asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
 }
@@ -388,25 +295,22 @@ struct Cfg {
     static constexpr int HALVES = TT / 64;                 // 64-token halves of a tile
     static constexpr int NJ = D / 8;                       // 1 KiB load instructions per K (and per V) tile
     static constexpr int NJH = NJ / HALVES;                // K load instructions per half (one per channel group)
-    static constexpr int NC = D / 8;                       // 8-channel fp16 chunks of a K row in the scores
     static constexpr int NH = D / 64;                      // 64-channel halves (PV: lane = channel)
-    static constexpr int HPW = (NREP % 2 == 0) ? 2 : 1;   // query heads per compute wave
-    static constexpr int WPT = NREP / HPW;                 // compute waves, sharing every tile
+    static constexpr int CW = 2;                           // compute waves: each takes half of every tile's tokens
+    static constexpr int NB = TT / 16, KS = D / 32, CB = D / 16, PS = TT / 32;  // matrix-core product shapes
     static constexpr int TPB = BS >= TT ? 1 : TT / BS;     // blocks per tile
     static constexpr int TILE = TT * D * E / 2;            // LDS halves per K (or V) tile
     static constexpr int QC = NREP * D / 8;                // 16-byte chunks of a group's queries
     static constexpr int QI = (QC + 63) / 64;              // q load instructions
     static constexpr int QBUF = QI * 64 * 8;               // halves per q buffer
-    static constexpr int THREADS = 64 * (WPT + 1);         // the compute waves and one load wave
+    static constexpr int THREADS = 64 * (CW + 1);          // the compute waves and one load wave
     static_assert(TPB <= 8, "block size of at least 16 tokens");
 };
 
-// decode_kernel: persistent, one workgroup per slot: WPT compute waves (one
-// per two query heads of the group, or one for a single head), which all read
-// every tile, each for its own query heads, and one load wave that issues
-// every tile load and waits for it. A wave that issues a
-// load stalls whenever the memory system is saturated; keeping all loads in
-// their own wave keeps those stalls off the compute waves.
+// decode_kernel: persistent, one workgroup per slot: two compute waves and
+// one load wave (wave 2) that issues every tile load and waits for it. A wave
+// that issues a load stalls whenever the memory system is saturated; keeping
+// all loads in their own wave keeps those stalls off the compute waves.
 //
 // Tile pipeline (step j computes tile position P_j; buffers alternate by j):
 //   prologue:  load wave issues K(P0), V(P0)
@@ -420,18 +324,36 @@ struct Cfg {
 // boundaries as well. The query of a unit is loaded into LDS with the K tile
 // of its first position.
 //
-// Layouts (fp16 pools, 64-token tiles): the K tile in LDS is [NJ][64
-// tokens][8 ch] (lane = token for QK); the V tile is [NJ row blocks][8
-// chunks][8 rows][8 tokens], loaded so that a load instruction still covers
-// eight whole 128-byte rows of V. PV uses lane = channel: lane ch reads the 8
-// chunks of its channel's 64 tokens, odd row blocks in the order c^1, which
-// keeps every 16-lane phase of the LDS read on distinct banks. The p vector
-// of a head (fp16, one per tile token) is broadcast from LDS. A lane thus
-// owns whole output channels: no cross-lane reduction of the output at all.
-// E4M3 pools, 128-token tiles: the K tile is [2 halves][D/16][64 tokens][16
-// ch] bytes (lane = token of each half); the V tile's bytes sit exactly as an
-// fp16 tile's, each 16-byte unit now 16 tokens of one row, and PV widens each
-// unit to two fp16 chunks.
+// Token split: compute wave w takes the w-th half of every tile's tokens
+// (16-token score blocks w*NB/2 .., 32-token output steps w*PS/2 ..) and
+// keeps its own online softmax state (max, sum, output) for all of the
+// group's query heads. At the end of a run of tiles of one (row, KV head),
+// wave 1 hands its state to wave 0 through LDS, and wave 0 rescales both to
+// the common max and adds them: the exact two-way merge of partial softmax
+// results.
+//
+// Register layouts (query head hq = lane % 16, lane group lg = lane / 16):
+// a score block's result holds tokens 4lg .. 4lg+3 of the block for head hq,
+// so a head's softmax state lives in lanes hq, hq+16, hq+32, hq+48 (their
+// max and sum combined with the permlane swaps); the fp16 probabilities of a
+// 32-token output step are already the B operand of V^T.P^T in the lanes
+// that computed them; the output accumulators hold head hq, channels
+// 16cb + 4lg .. 16cb + 4lg + 3.
+//
+// LDS tile layouts (fp16 pools, 64-token tiles): K is [NJ][64 tokens][8 ch],
+// so the A operand of a score product (token, 8 channels) is one 16-byte
+// read; V is [NJ row blocks][8 chunks][8 rows][8 tokens], loaded so that a
+// load instruction still covers eight whole 128-byte rows of V, and the A
+// operand of an output product (channel, 4 + 4 tokens) is two 8-byte reads.
+// E4M3 pools, 128-token tiles: K is [2 halves][D/16][64 tokens][16 ch] bytes,
+// one 16-byte read serving two score products after widening; V's bytes sit
+// exactly as an fp16 tile's, each 16-byte unit now 16 tokens of one row.
+//
+// Probabilities enter the output product as 2^15 * exp2(s - max) in fp16:
+// the factor cancels between output and sum. Weights down to 2^-29 of the
+// row's largest stay normal fp16 numbers (relative precision 2^-11), those
+// down to 2^-39 are subnormals, and smaller ones are 0; a plain
+// exp2(s - max) would already turn subnormal below 2^-14.
 //
 // Results: a one-partition row writes fp16 output directly; otherwise the
 // partition writes (max, sum, unnormalised output) with coherent stores and is
@@ -446,7 +368,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     float* __restrict__ part_acc, int B, int Hkv, int W, int N, int C, int P, float scale_log2, int width, float k_scale, float v_scale,
     float k_inv, float v_inv) {
     using K = Cfg<BS, D, NREP, F8>;
-    constexpr int NJ = K::NJ, NC = K::NC, NH = K::NH, WPT = K::WPT, HPW = K::HPW, TPB = K::TPB;
+    constexpr int NJ = K::NJ, NH = K::NH, CW = K::CW, TPB = K::TPB;
+    constexpr int NB = K::NB, KS = K::KS, CB = K::CB, PS = K::PS;
     constexpr int E = K::E, G16 = K::G16, TT = K::TT, HALVES = K::HALVES, NJH = K::NJH;
     constexpr int TILE = K::TILE, QC = K::QC, QI = K::QI, QBUF = K::QBUF, THREADS = K::THREADS;
     static_assert(BS % 16 == 0, "block size must be a multiple of 16");
@@ -454,7 +377,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_v[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[2][QBUF];
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[WPT][HPW][TT];
+    __shared__ __attribute__((aligned(16))) float s_xacc[K::CB * 4 * 64];  // wave 1's state at a run's end
+    __shared__ float s_xml[2 * 16];
     __shared__ __attribute__((aligned(16))) uint16_t s_kn[2][D];  // fused append: the new token's K ...
     __shared__ __attribute__((aligned(16))) uint16_t s_vn[2][D];  // ... and V, staged with the tile holding it
     __shared__ int s_len[kMaxRows];
@@ -466,8 +390,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wip = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in the workgroup
-    const bool loader = wip == WPT;                             // the load wave
-    const int h0 = wip * HPW;                                   // a compute wave's first query head
+    const bool loader = wip == CW;                              // the load wave
     const int Hq = Hkv * NREP;
     const int G = gridDim.x;
     const int cap = W * BS;
@@ -631,10 +554,12 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         vm_count += NJ;
     };
 
-    // ---- per-unit state
-    constexpr int QR = NC / 4;
-    unsigned qr[HPW][QR];
-    float m[HPW], lsum[HPW], acc[HPW][NH];
+    // ---- per-unit state of a compute wave (query head hq = lane % 16, lane group lg = lane / 16)
+    const int hq = lane & 15, lg = lane >> 4;
+    u32x4 qb[KS];
+    f32x4 acc[CB];
+    u32x4 pb[PS / 2];  // this tile's probabilities (this wave's tokens) as the output product's operand
+    float m = -INFINITY, lsum = 0.f;
 
     // The first tile is requested as soon as its table entries are in; the
     // entries of the next positions are requested after it.
@@ -699,85 +624,94 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         const Pos P3 = pos_at(P2.t + 1, P2, true);
         if (!loader && tile) {
             if (P0.first) {
-                const unsigned* qw = reinterpret_cast<const unsigned*>(&s_q[P0.k & 1][0]) + h0 * (D / 2);
+                // the query operand: head hq, channels c0(ks) .. c0(ks)+7 (zero past the group's heads)
+                const uint16_t* qh = &s_q[P0.k & 1][min(hq, NREP - 1) * D];  // rows past NREP: read, then zeroed
 #pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int i = 0; i < QR; ++i) qr[h][i] = qw[h * (D / 2) + 16 * i + (lane & 15)];
-#pragma unroll
-                for (int h = 0; h < HPW; ++h) {
-                    m[h] = -INFINITY;
-                    lsum[h] = 0.f;
-#pragma unroll
-                    for (int c = 0; c < NH; ++c) acc[h][c] = 0.f;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int c0 = F8 ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1) : 32 * ks + 8 * lg;
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(qh + c0);
+                    qb[ks] = hq < NREP ? x : u32x4{0u, 0u, 0u, 0u};
                 }
+                m = -INFINITY;
+                lsum = 0.f;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            // ---- scores: lane = token of each 64-token half, query pairs
-            // broadcast across lanes by DPP (an E4M3 tile: each 16-channel
-            // chunk is widened to two fp16 chunks as it is used)
-            const int t0 = P0.tile * TT;
-            float s[HALVES][HPW];
+            // ---- scores: S^T = K . Q^T per 16-token block. Every operand read of the
+            // tile is issued first (they complete in order), then the products, the
+            // blocks' chains interleaved.
+            constexpr int NB2 = NB / 2;   // this wave's 16-token blocks: wip*NB2 ..
+            constexpr int PS2 = PS / 2;   // and output steps: wip*PS2 ..
+            const int nb0 = wip * NB2;
+            f32x4 sc[NB2];
 #pragma unroll
-            for (int hf = 0; hf < HALVES; ++hf) {
-                u32x4 kj[NJH];
+            for (int nb = 0; nb < NB2; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (!F8) {
+                u32x4 kr[KS][NB2];
 #pragma unroll
-                for (int jj = 0; jj < NJH; ++jj)
-                    kj[jj] = *reinterpret_cast<const u32x4*>(&s_k[buf][(hf * NJH + jj) * 512 + lane * 8]);
-                float a4[4][HPW];
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                    for (int nb = 0; nb < NB2; ++nb)
+                        kr[ks][nb] = *reinterpret_cast<const u32x4*>(
+                            &s_k[buf][((4 * ks + lg) * 64 + 16 * (nb0 + nb) + hq) * 8]);
 #pragma unroll
-                    for (int h = 0; h < HPW; ++h) a4[k][h] = 0.f;
-                [&]<int... J>(std::integer_sequence<int, J...>) {
-                    ([&] {
-                        unsigned qj[HPW];
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                        for (int h = 0; h < HPW; ++h) qj[h] = qr[h][J / 4];
-                        if constexpr (F8)
-                            score_block<4 * (J % 4)>(a4, qj, widen8<J % 2>(kj[J / 2]));
-                        else
-                            score_block<4 * (J % 4)>(a4, qj, kj[J]);
-                    }(), ...);
-                }(std::make_integer_sequence<int, NC>{});
-                const bool live = t0 + 64 * hf + lane < P0.L;
+                    for (int nb = 0; nb < NB2; ++nb) sc[nb] = mfma16(kr[ks][nb], qb[ks], sc[nb]);
+                // all operand reads first, then the products
+                __builtin_amdgcn_sched_group_barrier(0x100, KS * NB2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, KS * NB2, 0);
+            } else {
+                // token 16(nb%4) + hq of 64-token half nb/4; one 16-byte read serves steps 2kp, 2kp+1
+                const char* kt = reinterpret_cast<const char*>(&s_k[buf][0]);
+                u32x4 kr[KS / 2][NB2];
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) {
-                    const float d = (a4[0][h] + a4[1][h]) + (a4[2][h] + a4[3][h]);
-                    s[hf][h] = live ? d * scale_log2 : -INFINITY;
+                for (int kp = 0; kp < KS / 2; ++kp)
+#pragma unroll
+                    for (int nb = 0; nb < NB2; ++nb)
+                        kr[kp][nb] = *reinterpret_cast<const u32x4*>(
+                            kt + ((nb0 + nb) >> 2) * (D * 64) + ((4 * kp + lg) * 64 + 16 * ((nb0 + nb) & 3) + hq) * 16);
+#pragma unroll
+                for (int kp = 0; kp < KS / 2; ++kp)
+#pragma unroll
+                    for (int nb = 0; nb < NB2; ++nb) {
+                        sc[nb] = mfma16(widen8<0>(kr[kp][nb]), qb[2 * kp], sc[nb]);
+                        sc[nb] = mfma16(widen8<1>(kr[kp][nb]), qb[2 * kp + 1], sc[nb]);
+                    }
+            }
+            // ---- online softmax (exp2 domain): max over the lane's 4*NB tokens, then over the
+            // four lanes of the head
+            const int t0 = P0.tile * TT + 16 * nb0 + 4 * lg;  // token of element 0 of this wave's block 0
+            float smax = -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = t0 + 16 * nb + i < P0.L ? sc[nb][i] * scale_log2 : -INFINITY;
+                    sc[nb][i] = x;
+                    smax = fmaxf(smax, x);
                 }
-                if constexpr (HALVES > 1) __builtin_amdgcn_sched_barrier(0);  // one half's K chunks live at a time
-            }
-            // ---- online softmax (exp2 domain)
-            float alpha[HPW];
-            bool rescale = false;
+            const float mn = fmaxf(m, cross_rows(smax, [](float a, float b) { return fmaxf(a, b); }));
+            const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
+            const float alpha = __builtin_amdgcn_exp2f(m - mref);
+            m = mn;
+            const float mb = mref - 15.f;  // p enters the products as 2^15 * exp2(s - max)
+            float ps = 0.f;
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-                float smax = s[0][h];
+            for (int q2 = 0; q2 < PS2; ++q2) {
+                _Float16 ph[8];
 #pragma unroll
-                for (int hf = 1; hf < HALVES; ++hf) smax = fmaxf(smax, s[hf][h]);
-                const float mn = fmaxf(m[h], wave_max(smax));
-                const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
-                alpha[h] = __builtin_amdgcn_exp2f(m[h] - mref);
-                rescale |= alpha[h] != 1.0f;
-                m[h] = mn;
-                float ps = 0.f;
-                // p enters PV and the sum as 2^15 * exp2(s - max) in fp16: the factor cancels in
-                // their ratio, and fp16 keeps its full 11-bit precision for scores down to 29
-                // (log2 units) below the running max instead of 14, subnormal p down to 39
-                const float mp = mref - 15.f;
-#pragma unroll
-                for (int hf = 0; hf < HALVES; ++hf) {
-                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[hf][h] - mp);
-                    ps += (float)ph;
-                    s_p[wip][h][64 * hf + lane] = ph;
+                for (int i = 0; i < 8; ++i) {
+                    ph[i] = (_Float16)__builtin_amdgcn_exp2f(sc[2 * q2 + (i >> 2)][i & 3] - mb);
+                    ps += (float)ph[i];
                 }
-                lsum[h] = lsum[h] * alpha[h] + ps;
+                pb[q2] = u32x4{pack_h2(ph[0], ph[1]), pack_h2(ph[2], ph[3]), pack_h2(ph[4], ph[5]),
+                               pack_h2(ph[6], ph[7])};
             }
-            if (__builtin_amdgcn_readfirstlane((int)rescale)) {
+            lsum = lsum * alpha + ps;
+            if (__builtin_amdgcn_readfirstlane((int)(__ballot(alpha != 1.0f) != 0))) {
 #pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int c = 0; c < NH; ++c) acc[h][c] *= alpha[h];
+                for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -838,107 +772,120 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             issue_k(P2, buf);
             if (buf) mk1 = vm_count; else mk0 = vm_count;
         }
-        if (!F8 && !loader && tile) {
-            // ---- PV: lane = channel; chunk c of the tile read in the order c ^ par
-            const int t0 = P0.tile * TT;
-            const int par = vc & 1;  // parity of this lane's row block (lane / 8)
-            const uint16_t* vb = &s_v[buf][(lane >> 3) * 512 + drow * 8];
-            const _Float16* pb = &s_p[wip][0][0];
-            // every LDS read of the phase first (one latency), then the dot products
-            u32x4 pv[8][HPW], vv[8][NH];
+        if (!loader && tile) {
+            // ---- output: O^T += V^T . P^T per 16-channel block, 32 tokens a step; lane l reads
+            // channel 16cb + hq, tokens 32ps + 4lg + 0..3 and 32ps + 16 + 4lg + 0..3
+            const int c7 = hq & 7;
+            if constexpr (!F8) {
+                // halves of (channel c, token t): (c/8)*512 + (t/8)*64 + (c%8)*8 + t%8
+                constexpr int PS2 = PS / 2;
+                const int q0 = wip * PS2;
+                const int tl = P0.L - P0.tile * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
+                const bool ragged = P0.tile * TT + TT > P0.L;
+                uint2 vr[PS2][CB][2];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int cc = c ^ par;  // the chunk this lane reads at step c
+                for (int q2 = 0; q2 < PS2; ++q2)
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) pv[c][h] = *reinterpret_cast<const u32x4*>(pb + h * TT + 8 * cc);
-#pragma unroll
-                for (int hv = 0; hv < NH; ++hv) vv[c][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8 * 512 + cc * 64);
-            }
-            if (t0 + TT > P0.L) {  // tokens past the row's end may hold NaN: zero their V
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const u32x4 mask = keep_first(P0.L - (t0 + 8 * (c ^ par)));
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) vv[c][hv] &= mask;
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-#pragma unroll
-                for (int hv = 0; hv < NH; ++hv)
-#pragma unroll
-                    for (int h = 0; h < HPW; ++h) acc[h][hv] = dot8(pv[c][h], vv[c][hv], acc[h][hv]);
-        }
-        if (F8 && !loader && tile) {
-            // ---- PV over an E4M3 tile of 128 tokens: lane = channel. The tile's
-            // bytes sit as the fp16 tile's do: instruction c/8, then 8 chunks
-            // of 16 tokens, each 8 rows of 16 bytes; chunk k read at step
-            // k ^ par, as above. Codes past the row's end were zeroed in LDS
-            // by the load wave.
-            const int par = vc & 1;
-            const char* vb = reinterpret_cast<const char*>(&s_v[buf][0]) + (lane >> 3) * 1024 + drow * 16;
-            const _Float16* pb = &s_p[wip][0][0];
-            // two groups of four chunks, each group's LDS reads issued together;
-            // the scheduling barrier keeps the second group's reads (and
-            // registers) out of the first group's arithmetic
-#pragma unroll
-            for (int grp = 0; grp < 2; ++grp) {
-                u32x4 vr[4][NH], pv[4][2][HPW];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int kk = (4 * grp + k) ^ par;  // tokens 16kk .. 16kk+15
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv)
-                        vr[k][hv] = *reinterpret_cast<const u32x4*>(vb + hv * 8192 + kk * 128);
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int h = 0; h < HPW; ++h)
-                            pv[k][c][h] = *reinterpret_cast<const u32x4*>(pb + h * TT + 16 * kk + 8 * c);
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) {
-                        const u32x4 lo = widen8<0>(vr[k][hv]), hi = widen8<1>(vr[k][hv]);
-#pragma unroll
-                        for (int h = 0; h < HPW; ++h) {
-                            acc[h][hv] = dot8(pv[k][0][h], lo, acc[h][hv]);
-                            acc[h][hv] = dot8(pv[k][1][h], hi, acc[h][hv]);
-                        }
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const uint16_t* v = &s_v[buf][(2 * cb + (hq >> 3)) * 512 + (4 * (q0 + q2) + (lg >> 1)) * 64 +
+                                                      c7 * 8 + 4 * (lg & 1)];
+                        vr[q2][cb][0] = *reinterpret_cast<const uint2*>(v);
+                        vr[q2][cb][1] = *reinterpret_cast<const uint2*>(v + 128);
                     }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (!loader && P0.last) {
-            // ---- the unit's result
-            const int b = P0.b, g = P0.g;
-            float lt[HPW];
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) lt[h] = tile ? wave_sum(lsum[h]) : 1.f;
-            if (P0.np == 1) {
-                uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + h0) * D + lane;
-#pragma unroll
-                for (int h = 0; h < HPW; ++h)
-#pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) {
-                        const float o = tile ? acc[h][hv] / lt[h] * v_scale : 0.f;
-                        st_u16(orow + h * D + hv * 64, __builtin_bit_cast(uint16_t, (_Float16)o));
+                for (int q2 = 0; q2 < PS2; ++q2) {
+                    unsigned mlo0 = ~0u, mlo1 = ~0u, mhi0 = ~0u, mhi1 = ~0u;
+                    if (ragged) {  // tokens past the row's end may hold NaN: zero their V
+                        mlo0 = keep2(tl - 32 * q2, 0);
+                        mlo1 = keep2(tl - 32 * q2, 2);
+                        mhi0 = keep2(tl - 32 * q2 - 16, 0);
+                        mhi1 = keep2(tl - 32 * q2 - 16, 2);
                     }
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[cb] = mfma16(u32x4{vr[q2][cb][0].x & mlo0, vr[q2][cb][0].y & mlo1, vr[q2][cb][1].x & mhi0,
+                                               vr[q2][cb][1].y & mhi1},
+                                         pb[q2], acc[cb]);
+                }
             } else {
-                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.slot) * NREP + h0;
-                float* pa = part_acc + slot * D + lane;
+                // bytes of (channel c, token t): (c/8)*1024 + (t/16)*128 + (c%8)*16 + t%16; codes of
+                // tokens past the row's end (possibly NaN) are zeroed in registers
+                const char* vt = reinterpret_cast<const char*>(&s_v[buf][0]);
+                constexpr int PS2 = PS / 2;
+                const int q0 = wip * PS2;
+                const int tl = P0.L - P0.tile * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
+                const bool ragged = P0.tile * TT + TT > P0.L;
+                auto keep4 = [](int n) { return n >= 4 ? ~0u : (n <= 0 ? 0u : (1u << (8 * n)) - 1u); };
+                unsigned vr[PS2][CB][2];
 #pragma unroll
-                for (int h = 0; h < HPW; ++h)
+                for (int q2 = 0; q2 < PS2; ++q2)
 #pragma unroll
-                    for (int hv = 0; hv < NH; ++hv) st_f32_sc1(pa + h * D + hv * 64, acc[h][hv]);
-                float* pm = part_ml + slot * 2;
-                if (lane == 0) {
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const char* v = vt + (2 * cb + (hq >> 3)) * 1024 + (2 * (q0 + q2)) * 128 + c7 * 16 + 4 * lg;
+                        vr[q2][cb][0] = *reinterpret_cast<const unsigned*>(v);
+                        vr[q2][cb][1] = *reinterpret_cast<const unsigned*>(v + 128);
+                    }
 #pragma unroll
-                    for (int h = 0; h < HPW; ++h) st_2f32_sc1(pm + 2 * h, m[h], lt[h]);
+                for (int q2 = 0; q2 < PS2; ++q2)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const unsigned w0 = vr[q2][cb][0] & (ragged ? keep4(tl - 32 * q2) : ~0u);
+                        const unsigned w1 = vr[q2][cb][1] & (ragged ? keep4(tl - 32 * q2 - 16) : ~0u);
+                        acc[cb] = mfma16(u32x4{f8x2<false>(w0), f8x2<true>(w0), f8x2<false>(w1), f8x2<true>(w1)},
+                                         pb[q2], acc[cb]);
+                    }
+            }
+        }
+        float lt = 0.f;
+        if (P0.last) {
+            // ---- the two compute waves' states of this run combined (wave 1 -> LDS -> wave 0)
+            if (!loader) lt = tile ? cross_rows(lsum, [](float a, float c) { return a + c; }) : 0.f;
+            if (wip == 1) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    *reinterpret_cast<f32x4*>(&s_xacc[(cb * 64 + lane) * 4]) = tile ? acc[cb] : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (lg == 0) {
+                    s_xml[hq] = tile ? m : -INFINITY;
+                    s_xml[16 + hq] = lt;
                 }
-                if (wip == 0 && lane == 0) {
+            }
+            __syncthreads();
+            if (wip == 0 && tile) {
+                const float m1 = s_xml[hq], l1 = s_xml[16 + hq];
+                const float mn = fmaxf(m, m1);
+                const float mr = mn == -INFINITY ? 0.f : mn;
+                const float a0 = __builtin_amdgcn_exp2f(m - mr), a1 = __builtin_amdgcn_exp2f(m1 - mr);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[cb] = acc[cb] * a0 + *reinterpret_cast<const f32x4*>(&s_xacc[(cb * 64 + lane) * 4]) * a1;
+                lt = lt * a0 + l1 * a1;
+                m = mn;
+            }
+        }
+        if (wip == 0 && P0.last) {
+            // ---- the unit's result: head hq, channels 16cb + 4lg + 0..3
+            const int b = P0.b, g = P0.g;
+            if (!tile) lt = 1.f;
+            if (P0.np == 1) {
+                if (hq < NREP) {
+                    uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + hq) * D + 4 * lg;
+                    const float r = v_scale / lt;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const f32x4 o = tile ? acc[cb] * r : f32x4{0.f, 0.f, 0.f, 0.f};
+                        st_b64(orow + 16 * cb, pack_h2((_Float16)o[0], (_Float16)o[1]),
+                               pack_h2((_Float16)o[2], (_Float16)o[3]));
+                    }
+                }
+            } else {
+                const size_t slot = ((size_t)(b * Hkv + g) * P + P0.slot) * NREP + hq;
+                if (hq < NREP) {
+                    float* pa = part_acc + slot * D + 4 * lg;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) st_f32x4_sc1(pa + 16 * cb, tile ? acc[cb] : f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (lg == 0) st_2f32_sc1(part_ml + slot * 2, m, lt);
+                }
+                if (lane == 0) {
                     const int n = s_npend;
                     if (n < kMaxPending) {
                         s_pend[n] = b * Hkv + g;
