@@ -246,9 +246,10 @@ pa_status paged_decode_attn_masked(uint16_t *out, const uint16_t *q, const uint1
  * "The architecture: every piece explained": the manager clones the one
  * shared block a sequence must write into and repoints that sequence's table
  * entry, leaving the readers untouched; "End-to-end flow"; PagedAttention,
- * "Sharing is the part that pays twice": a reference count and copy-on-write
- * for the block that diverges]. Which blocks to copy is the caller's
- * bookkeeping (paged_kv_cache_06_amd.blocks.plan_copy_on_write does it on the
+ * "Sharing is the part that pays twice": a shared block counts its readers,
+ * and only the one that a row starts to change is copied for that row]. Which
+ * blocks to copy is the caller's bookkeeping
+ * (paged_kv_cache_06_amd.blocks.plan_copy_on_write does it on the
  * host); run the copies before the step's kv_append.
  *
  * src, dst: device int32 [num_pairs]. A pair with an id outside [0, N), or
@@ -266,9 +267,9 @@ pa_status kv_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src,
 
 /*
  * kv_scatter_prefill -- after a prefill, move each row's prompt K/V into its
- * blocks [Paged attention, "What changed": newly admitted requests are
- * prefilled together, left padded to the group's widest prompt, and each
- * row's KV is then copied into its blocks with the padding dropped].
+ * blocks [Paged attention, "What changed": requests admitted together run
+ * one prefill, their prompts padded on the left to the longest of them; each
+ * row's keys and values then go into its own blocks without the padding].
  *
  * k_src, v_src: [num_seqs][Hkv][S][D] fp16 (S = padded_len, token-major rows
  * of D channels), 16-byte aligned; row b's prompt of length P =

@@ -357,9 +357,9 @@ struct Cfg {
 //
 // Results: a one-partition row writes fp16 output directly; otherwise the
 // partition writes (max, sum, unnormalised output) with coherent stores and is
-// listed; at exit the workgroup adds the number of partitions it finished of
-// each (row, KV head) to that pair's arrival counter in one atomic, and merges
-// every pair whose count it completed, in partition order.
+// listed; at exit the workgroup adds one to the arrival counter of each
+// (row, KV head) it holds a partition of, and merges every pair whose count
+// it completed, in partition order.
 template <int BS, int D, int NREP, bool F8>
 __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* k_pool, uint16_t* v_pool,
