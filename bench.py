@@ -94,11 +94,23 @@ def _code_only(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
+def _compile_flags() -> list:
+    """The hipcc flags the library is built with (read from the build module's file)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_pa_build", os.path.join(ROOT, "paged_kv_cache_06_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return list(mod.HIPCC_FLAGS)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the decode kernel's code (comments and blank lines aside) and of
+    the compiler flags: a change of either voids the committed counter records."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path) as f:
             h.update(_code_only(f.read()).encode())
+    h.update(" ".join(_compile_flags()).encode())
     return h.hexdigest()[:16]
 
 

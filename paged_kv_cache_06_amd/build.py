@@ -31,6 +31,11 @@ HIPCC_FLAGS = [
     "-fPIC",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the decode kernel's accumulators are
+    # also read and scaled by vector instructions, and with the default choice
+    # (accumulation registers) every product was bracketed by copies in and out,
+    # which serialised the eight output products of a step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
