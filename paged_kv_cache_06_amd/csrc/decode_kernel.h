@@ -258,22 +258,35 @@ constexpr int kLenNoSlot = 0x40000000;   // ... and a flag: the length exceeds t
 // at least C tiles, which bounds the partials of a (row, KV head) by the
 // workspace's P.
 struct Pos {
+    // Packed so that the positions in flight take few scalar registers:
+    //   tf:  tile index within the row (bits 0-23; rows hold at most 2^30 tokens),
+    //        flags first (24) and last (25) tile of the run, ap (26): the row takes
+    //        this step's new token (fused append; L >= 1, within the table), nw (27):
+    //        this tile holds that token, kp (28): parity of the run's ordinal in
+    //        this workgroup (it picks the query buffer)
+    //   bgn: row (bits 0-7, < kMaxRows), KV head (8-20), partitions np of the
+    //        (row, KV head) (21-27, <= kMaxParts)
     int t;               // tile number in the batch; >= this workgroup's range end means none
-    int b, g;            // row, KV head
-    int tile;            // tile index within the row
-    int nt;              // tiles of the row (>= 1)
     int L;               // row length (0: an empty row's only, data-less tile)
-    int k;               // ordinal of the run within this workgroup
-    int np, slot;        // workgroups covering the (row, KV head), and this one's index among them
-    int first, last;     // the run's first / last tile
+    int nt;              // tiles of the row (>= 1)
+    int tf, bgn;
+    int slot;            // this workgroup's index among the np
     int e0, e1, e2, e3;  // physical blocks of the tile (e1.. used when blocks are shorter than a tile)
     int e4, e5, e6, e7;
-    int ap;              // the row takes this step's new token (fused append; L >= 1, within the table)
-    int nw;              // this tile holds that token (the row's last tile of an appending row)
-    int enew;            // physical block of that token (read by the wave that stores it)
+    int enew;            // physical block of the new token (read by the wave that stores it)
     __device__ bool valid(int t_end) const { return t < t_end; }
     __device__ bool has_tile() const { return L > 0; }
+    __device__ int tile() const { return tf & 0xffffff; }
+    __device__ int first() const { return (tf >> 24) & 1; }
+    __device__ int last() const { return (tf >> 25) & 1; }
+    __device__ int ap() const { return (tf >> 26) & 1; }
+    __device__ int nw() const { return (tf >> 27) & 1; }
+    __device__ int kp() const { return (tf >> 28) & 1; }
+    __device__ int b() const { return bgn & 0xff; }
+    __device__ int g() const { return (bgn >> 8) & 0x1fff; }
+    __device__ int np() const { return (bgn >> 21) & 0x7f; }
 };
+static_assert(kMaxRows <= 256 && kMaxParts < 128, "Pos field widths");
 
 // Row of tile u: the last row whose prefix count is <= u, by two rounds of a
 // 64-lane search over the LDS prefix array pre[0..B].
@@ -443,8 +456,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     auto load_entries = [&](Pos& s) {
         s.e0 = s.e1 = s.e2 = s.e3 = s.e4 = s.e5 = s.e6 = s.e7 = 0;
         if (!loader || !s.valid(t_end) || !s.has_tile()) return;
-        const int32_t* trow = tables + (size_t)s.b * W;
-        const int n0 = (s.tile * TT) / BS;
+        const int32_t* trow = tables + (size_t)s.b() * W;
+        const int n0 = (s.tile() * TT) / BS;
         const int nblk = ((width > 0 ? max(s.L, width) : s.L) + BS - 1) / BS;
         auto at = [&](int i) { return trow[n0 + i < nblk ? n0 + i : n0]; };
         s.e0 = trow[n0];
@@ -468,32 +481,37 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             s.t = t_end;
             return s;
         }
-        if (has_prev && prev.tile + 1 < prev.nt) {  // the same run goes on
+        int tile, first, ap, kp;
+        if (has_prev && prev.tile() + 1 < prev.nt) {  // the same run goes on
             s = prev;
             s.t = t;
-            s.tile = prev.tile + 1;
-            s.first = 0;
+            tile = prev.tile() + 1;
+            first = 0;
+            ap = prev.ap();
+            kp = prev.kp();
         } else {
             s.t = t;
-            s.b = find_row(s_pre, B, t, lane);
-            const int lf = __builtin_amdgcn_readfirstlane(s_len[s.b]);
+            const int b = find_row(s_pre, B, t, lane);
+            const int lf = __builtin_amdgcn_readfirstlane(s_len[b]);
             s.L = lf & kLenMask;
-            s.ap = append && s.L > 0 && !(lf & kLenNoSlot);
+            ap = append && s.L > 0 && !(lf & kLenNoSlot);
             s.nt = max(1, ((width > 0 && s.L > 0 ? max(width, s.L) : s.L) + TT - 1) / TT);
-            const int r = t - __builtin_amdgcn_readfirstlane(s_pre[s.b]);
-            s.g = r / s.nt;
-            s.tile = r - s.g * s.nt;
-            const int a0 = t - s.tile;  // the (row, KV head)'s first tile
+            const int r = t - __builtin_amdgcn_readfirstlane(s_pre[b]);
+            const int g = r / s.nt;
+            tile = r - g * s.nt;
+            const int a0 = t - tile;  // the (row, KV head)'s first tile
             const int w0 = owner(a0);
-            s.np = owner(a0 + s.nt - 1) - w0 + 1;
+            const int np = owner(a0 + s.nt - 1) - w0 + 1;
             s.slot = w - w0;
-            s.k = has_prev ? prev.k + 1 : 0;
-            s.first = 1;
+            s.bgn = b | (g << 8) | (np << 21);
+            kp = has_prev ? prev.kp() ^ 1 : 0;
+            first = 1;
         }
-        s.last = (t + 1 == t_end) || (s.tile + 1 == s.nt);
-        s.nw = s.ap && s.tile == (s.L - 1) / TT;
+        const int last = (t + 1 == t_end) || (tile + 1 == s.nt);
+        const int nw = ap && tile == (s.L - 1) / TT;
+        s.tf = tile | (first << 24) | (last << 25) | (ap << 26) | (nw << 27) | (kp << 28);
         s.enew = 0;
-        if (wip == 0 && s.nw) s.enew = tables[(size_t)s.b * W + (s.L - 1) / BS];
+        if (wip == 0 && nw) s.enew = tables[(size_t)s.b() * W + (s.L - 1) / BS];
         load_entries(s);
         return s;
     };
@@ -516,26 +534,26 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     const unsigned lds_kn = lds_addr(&s_kn[0][0]), lds_vn = lds_addr(&s_vn[0][0]);
     // the new token's K (or V) of a tile that holds it, staged in LDS ahead of the tile's own loads
     auto issue_new = [&](const Pos& s, const uint16_t* src, unsigned dst) {
-        if (lane < D / 8) dma16(src + ((size_t)s.b * Hkv + s.g) * D + 8 * lane, dst);
+        if (lane < D / 8) dma16(src + ((size_t)s.b() * Hkv + s.g()) * D + 8 * lane, dst);
         vm_count += 1;
     };
     auto issue_q = [&](const Pos& s) {
-        const uint16_t* qrow = q + ((size_t)s.b * Hq + (size_t)s.g * NREP) * D;
+        const uint16_t* qrow = q + ((size_t)s.b() * Hq + (size_t)s.g() * NREP) * D;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
             const int c = i * 64 + lane;
-            dma16(qrow + 8 * min(c, QC - 1), lds_q + (unsigned)(((s.k & 1) * QBUF + i * 512) * 2));
+            dma16(qrow + 8 * min(c, QC - 1), lds_q + (unsigned)(((s.kp()) * QBUF + i * 512) * 2));
         }
         vm_count += QI;
     };
     auto issue_k = [&](const Pos& s, int buf) {
-        if (s.nw) issue_new(s, k_new, lds_kn + (unsigned)(buf * D * 2));
+        if (s.nw()) issue_new(s, k_new, lds_kn + (unsigned)(buf * D * 2));
 #pragma unroll
         for (int hf = 0; hf < HALVES; ++hf) {  // lane = token of the half; one instruction per channel group
-            const int tok = s.tile * TT + 64 * hf + lane;
+            const int tok = s.tile() * TT + 64 * hf + lane;
             const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (64 * hf + lane) / BS), N);
             const char* src = reinterpret_cast<const char*>(k_pool) +
-                              ((size_t)phys * Hkv + s.g) * (size_t)(D * BS) * E + (size_t)(tok % BS) * 16;
+                              ((size_t)phys * Hkv + s.g()) * (size_t)(D * BS) * E + (size_t)(tok % BS) * 16;
 #pragma unroll
             for (int j = 0; j < NJH; ++j)
                 dma16(src + (size_t)j * (BS * 16), lds_k + (unsigned)((buf * TILE + (hf * NJH + j) * 512) * 2));
@@ -543,11 +561,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         vm_count += NJ;
     };
     auto issue_v = [&](const Pos& s, int buf) {
-        if (s.nw) issue_new(s, v_new, lds_vn + (unsigned)(buf * D * 2));
-        const int tok = s.tile * TT + G16 * vc;
+        if (s.nw()) issue_new(s, v_new, lds_vn + (unsigned)(buf * D * 2));
+        const int tok = s.tile() * TT + G16 * vc;
         const int phys = clamp_block(entry_for(s, TPB == 1 ? 0 : (G16 * vc) / BS), N);
         const char* src = reinterpret_cast<const char*>(v_pool) +
-                          (((size_t)phys * Hkv + s.g) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS)) * E;
+                          (((size_t)phys * Hkv + s.g()) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS)) * E;
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)  // rows 8jj .. 8jj+7
             dma16(src + (size_t)jj * (8 * BS) * E, lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
@@ -585,9 +603,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         auto new_k_slot = [&](int tn) {
             return reinterpret_cast<u32x4*>(&s_k[buf][((tn >> 6) * NJH + lane) * 512 + (tn & 63) * 8]);
         };
-        if (loader && tile && P0.nw) {  // fused append: the new token's K into its slot of the tile
+        if (loader && tile && P0.nw()) {  // fused append: the new token's K into its slot of the tile
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * TT;
+            const int tn = P0.L - 1 - P0.tile() * TT;
             if constexpr (!F8) {
                 if (lane < D / 8) *new_k_slot(tn) = *reinterpret_cast<const u32x4*>(&s_kn[buf][lane * 8]);
             } else {  // quantized, one channel per lane and half: byte c%16 of group c/16
@@ -603,16 +621,16 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             wait_lds();
         }
         tile_barrier();  // K(P_j) is in LDS for every wave; PV of step j-1 is done everywhere
-        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N && lane < D / G16) {
+        if (wip == 0 && tile && P0.nw() && (unsigned)P0.enew < (unsigned)N && lane < D / G16) {
             // fused append: the new token's K into the pool (nothing in this launch reads it back)
-            const size_t base = (size_t)P0.enew * Hkv + P0.g;
-            const int tn = P0.L - 1 - P0.tile * TT;
+            const size_t base = (size_t)P0.enew * Hkv + P0.g();
+            const int tn = P0.L - 1 - P0.tile() * TT;
             st_b128(reinterpret_cast<char*>(k_pool) + ((base * (D / G16) + lane) * BS + (P0.L - 1) % BS) * 16,
                     *new_k_slot(tn));
         }
         if (loader && P1.valid(t_end) && P1.has_tile()) {
             if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
-                if (P1.first) issue_q(P1);
+                if (P1.first()) issue_q(P1);
                 issue_k(P1, 1);
                 mk1 = vm_count;
             }
@@ -623,9 +641,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         // before anything waits on them
         const Pos P3 = pos_at(P2.t + 1, P2, true);
         if (!loader && tile) {
-            if (P0.first) {
+            if (P0.first()) {
                 // the query operand: head hq, channels c0(ks) .. c0(ks)+7 (zero past the group's heads)
-                const uint16_t* qh = &s_q[P0.k & 1][min(hq, NREP - 1) * D];  // rows past NREP: read, then zeroed
+                const uint16_t* qh = &s_q[P0.kp()][min(hq, NREP - 1) * D];  // rows past NREP: read, then zeroed
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int c0 = F8 ? 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1) : 32 * ks + 8 * lg;
@@ -681,7 +699,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             }
             // ---- online softmax (exp2 domain): max over the lane's 4*NB tokens, then over the
             // four lanes of the head
-            const int t0 = P0.tile * TT + 16 * nb0 + 4 * lg;  // token of element 0 of this wave's block 0
+            const int t0 = P0.tile() * TT + 16 * nb0 + 4 * lg;  // token of element 0 of this wave's block 0
             float smax = -INFINITY;
 #pragma unroll
             for (int nb = 0; nb < NB2; ++nb)
@@ -716,9 +734,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (loader && tile) wait_vmem_dyn(vm_count - (buf ? mv1 : mv0));
-        if (!F8 && loader && tile && P0.nw) {  // fused append: the new token's V into its slot of the tile
+        if (!F8 && loader && tile && P0.nw()) {  // fused append: the new token's V into its slot of the tile
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int tn = P0.L - 1 - P0.tile * TT;
+            const int tn = P0.L - 1 - P0.tile() * TT;
 #pragma unroll
             for (int hv = 0; hv < NH; ++hv) {
                 const int c = hv * 64 + lane;
@@ -731,20 +749,20 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             return reinterpret_cast<uint8_t*>(&s_v[buf][0]) + (c >> 3) * 1024 + ((tn >> 4) * 8 + (c & 7)) * 16 +
                    (tn & 15);
         };
-        if (F8 && loader && tile && (P0.tile * TT + TT > P0.L || P0.nw)) {
+        if (F8 && loader && tile && (P0.tile() * TT + TT > P0.L || P0.nw())) {
             // an E4M3 tile past the row's end: its dead slots may hold NaN
             // codes; they are zeroed in LDS here (lane = chunk*8 + row, one
             // 16-byte unit per instruction), so PV needs no masking; then
             // the fused append's new token (quantized) goes into its slot
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (P0.tile * TT + TT > P0.L) {
-                const u32x4 mask = keep_first_bytes(P0.L - (P0.tile * TT + 16 * vc));
+            if (P0.tile() * TT + TT > P0.L) {
+                const u32x4 mask = keep_first_bytes(P0.L - (P0.tile() * TT + 16 * vc));
                 char* vt = reinterpret_cast<char*>(&s_v[buf][0]) + 16 * lane;
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<u32x4*>(vt + jj * 1024) &= mask;
             }
-            if (P0.nw) {
-                const int tn = P0.L - 1 - P0.tile * TT;
+            if (P0.nw()) {
+                const int tn = P0.L - 1 - P0.tile() * TT;
                 const _Float16* x = reinterpret_cast<const _Float16*>(&s_vn[buf][0]);
                 const unsigned w = pa_e4m3::quantize2(x[lane], x[NH > 1 ? 64 + lane : lane], v_scale, v_inv);
 #pragma unroll
@@ -753,9 +771,9 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             wait_lds();
         }
         tile_barrier();  // V(P_j) is in LDS for every wave; every wave is done with K(P_j)
-        if (wip == 0 && tile && P0.nw && (unsigned)P0.enew < (unsigned)N) {
+        if (wip == 0 && tile && P0.nw() && (unsigned)P0.enew < (unsigned)N) {
             // fused append: the new token's V into the pool
-            const size_t base = (size_t)P0.enew * Hkv + P0.g;
+            const size_t base = (size_t)P0.enew * Hkv + P0.g();
             const int slot = (P0.L - 1) % BS;
 #pragma unroll
             for (int hv = 0; hv < NH; ++hv) {
@@ -764,11 +782,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     st_u16(v_pool + (base * D + c) * BS + slot, s_vn[buf][c]);
                 else
                     st_u8(reinterpret_cast<uint8_t*>(v_pool) + (base * D + c) * BS + slot,
-                          *v8_at(c, P0.L - 1 - P0.tile * TT));
+                          *v8_at(c, P0.L - 1 - P0.tile() * TT));
             }
         }
         if (loader && P2.valid(t_end) && P2.has_tile()) {
-            if (P2.first) issue_q(P2);
+            if (P2.first()) issue_q(P2);
             issue_k(P2, buf);
             if (buf) mk1 = vm_count; else mk0 = vm_count;
         }
@@ -780,8 +798,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 // halves of (channel c, token t): (c/8)*512 + (t/8)*64 + (c%8)*8 + t%8
                 constexpr int PS2 = PS / 2;
                 const int q0 = wip * PS2;
-                const int tl = P0.L - P0.tile * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
-                const bool ragged = P0.tile * TT + TT > P0.L;
+                const int tl = P0.L - P0.tile() * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
+                const bool ragged = P0.tile() * TT + TT > P0.L;
                 uint2 vr[PS2][CB][2];
 #pragma unroll
                 for (int q2 = 0; q2 < PS2; ++q2)
@@ -813,8 +831,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 const char* vt = reinterpret_cast<const char*>(&s_v[buf][0]);
                 constexpr int PS2 = PS / 2;
                 const int q0 = wip * PS2;
-                const int tl = P0.L - P0.tile * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
-                const bool ragged = P0.tile * TT + TT > P0.L;
+                const int tl = P0.L - P0.tile() * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
+                const bool ragged = P0.tile() * TT + TT > P0.L;
                 auto keep4 = [](int n) { return n >= 4 ? ~0u : (n <= 0 ? 0u : (1u << (8 * n)) - 1u); };
                 unsigned vr[PS2][CB][2];
 #pragma unroll
@@ -837,7 +855,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             }
         }
         float lt = 0.f;
-        if (P0.last) {
+        if (P0.last()) {
             // ---- the two compute waves' states of this run combined (wave 1 -> LDS -> wave 0)
             if (!loader) lt = tile ? cross_rows(lsum, [](float a, float c) { return a + c; }) : 0.f;
             if (wip == 1) {
@@ -862,11 +880,11 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 m = mn;
             }
         }
-        if (wip == 0 && P0.last) {
+        if (wip == 0 && P0.last()) {
             // ---- the unit's result: head hq, channels 16cb + 4lg + 0..3
-            const int b = P0.b, g = P0.g;
+            const int b = P0.b(), g = P0.g();
             if (!tile) lt = 1.f;
-            if (P0.np == 1) {
+            if (P0.np() == 1) {
                 if (hq < NREP) {
                     uint16_t* orow = out + ((size_t)b * Hq + (size_t)g * NREP + hq) * D + 4 * lg;
                     const float r = v_scale / lt;
@@ -889,7 +907,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     const int n = s_npend;
                     if (n < kMaxPending) {
                         s_pend[n] = b * Hkv + g;
-                        s_pend_np[n] = P0.np;
+                        s_pend_np[n] = P0.np();
                         s_npend = n + 1;
                     }
                 }
