@@ -473,8 +473,17 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             s.e7 = at(7);
         }
     };
-    // the position of tile t (prev: the position before it in this range)
-    auto pos_at = [&](int t, const Pos& prev, bool has_prev) {
+    // the partitions of a run's (row, KV head) and this workgroup's index among them
+    auto split_of = [&](Pos& s) {
+        const int a0 = s.t - s.tile();  // the (row, KV head)'s first tile
+        const int w0 = owner(a0);
+        const int np = owner(a0 + s.nt - 1) - w0 + 1;
+        s.slot = w - w0;
+        s.bgn = (s.bgn & 0x1fffff) | (np << 21);
+    };
+    // the position of tile t (prev: the position before it in this range); with
+    // defer, the start of a run leaves np and slot to split_of
+    auto pos_at = [&](int t, const Pos& prev, bool has_prev, bool defer = false) {
         Pos s;
         if (t >= t_end) {
             s = prev;
@@ -499,11 +508,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             const int r = t - __builtin_amdgcn_readfirstlane(s_pre[b]);
             const int g = r / s.nt;
             tile = r - g * s.nt;
-            const int a0 = t - tile;  // the (row, KV head)'s first tile
-            const int w0 = owner(a0);
-            const int np = owner(a0 + s.nt - 1) - w0 + 1;
-            s.slot = w - w0;
-            s.bgn = b | (g << 8) | (np << 21);
+            s.bgn = b | (g << 8);
+            if (!defer) split_of(s);
             kp = has_prev ? prev.kp() ^ 1 : 0;
             first = 1;
         }
@@ -582,7 +588,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     // The first tile is requested as soon as its table entries are in; the
     // entries of the next positions are requested after it.
     const Pos none = {};
-    Pos P0 = pos_at(t_begin, none, false);
+    Pos P0 = pos_at(t_begin, none, false, true);
     int mk0 = 0, mk1 = 0, mv0 = 0, mv1 = 0;  // vm_count after each buffer's last load
     if (loader && P0.valid(t_end) && P0.has_tile()) {
         issue_q(P0);
@@ -591,6 +597,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
         issue_v(P0, 0);
         mv0 = vm_count;
     }
+    if (P0.valid(t_end)) split_of(P0);  // after the first request: not needed for it
     Pos P1 = pos_at(t_begin + 1, P0, true);
     Pos P2 = pos_at(t_begin + 2, P1, true);
 
