@@ -817,30 +817,33 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                         vr[q2][cb][0] = *reinterpret_cast<const uint2*>(v);
                         vr[q2][cb][1] = *reinterpret_cast<const uint2*>(v + 128);
                     }
+                if (ragged) {  // tokens past the row's end may hold NaN: zero their V
 #pragma unroll
-                for (int q2 = 0; q2 < PS2; ++q2) {
-                    unsigned mlo0 = ~0u, mlo1 = ~0u, mhi0 = ~0u, mhi1 = ~0u;
-                    if (ragged) {  // tokens past the row's end may hold NaN: zero their V
-                        mlo0 = keep2(tl - 32 * q2, 0);
-                        mlo1 = keep2(tl - 32 * q2, 2);
-                        mhi0 = keep2(tl - 32 * q2 - 16, 0);
-                        mhi1 = keep2(tl - 32 * q2 - 16, 2);
+                    for (int q2 = 0; q2 < PS2; ++q2) {
+                        const unsigned mlo0 = keep2(tl - 32 * q2, 0), mlo1 = keep2(tl - 32 * q2, 2);
+                        const unsigned mhi0 = keep2(tl - 32 * q2 - 16, 0), mhi1 = keep2(tl - 32 * q2 - 16, 2);
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb) {
+                            vr[q2][cb][0].x &= mlo0;
+                            vr[q2][cb][0].y &= mlo1;
+                            vr[q2][cb][1].x &= mhi0;
+                            vr[q2][cb][1].y &= mhi1;
+                        }
                     }
+                }
+#pragma unroll
+                for (int q2 = 0; q2 < PS2; ++q2)
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[cb] = mfma16(u32x4{vr[q2][cb][0].x & mlo0, vr[q2][cb][0].y & mlo1, vr[q2][cb][1].x & mhi0,
-                                               vr[q2][cb][1].y & mhi1},
+                        acc[cb] = mfma16(u32x4{vr[q2][cb][0].x, vr[q2][cb][0].y, vr[q2][cb][1].x, vr[q2][cb][1].y},
                                          pb[q2], acc[cb]);
-                }
             } else {
-                // bytes of (channel c, token t): (c/8)*1024 + (t/16)*128 + (c%8)*16 + t%16; codes of
-                // tokens past the row's end (possibly NaN) are zeroed in registers
+                // bytes of (channel c, token t): (c/8)*1024 + (t/16)*128 + (c%8)*16 + t%16; the
+                // codes of tokens past the row's end are already zero (the load wave cleared them
+                // in LDS before barrier B)
                 const char* vt = reinterpret_cast<const char*>(&s_v[buf][0]);
                 constexpr int PS2 = PS / 2;
                 const int q0 = wip * PS2;
-                const int tl = P0.L - P0.tile() * TT - 32 * q0 - 4 * lg;  // live tokens from this lane's first one
-                const bool ragged = P0.tile() * TT + TT > P0.L;
-                auto keep4 = [](int n) { return n >= 4 ? ~0u : (n <= 0 ? 0u : (1u << (8 * n)) - 1u); };
                 unsigned vr[PS2][CB][2];
 #pragma unroll
                 for (int q2 = 0; q2 < PS2; ++q2)
@@ -854,8 +857,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 for (int q2 = 0; q2 < PS2; ++q2)
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        const unsigned w0 = vr[q2][cb][0] & (ragged ? keep4(tl - 32 * q2) : ~0u);
-                        const unsigned w1 = vr[q2][cb][1] & (ragged ? keep4(tl - 32 * q2 - 16) : ~0u);
+                        const unsigned w0 = vr[q2][cb][0], w1 = vr[q2][cb][1];
                         acc[cb] = mfma16(u32x4{f8x2<false>(w0), f8x2<true>(w0), f8x2<false>(w1), f8x2<true>(w1)},
                                          pb[q2], acc[cb]);
                     }
