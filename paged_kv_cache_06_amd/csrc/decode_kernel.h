@@ -708,14 +708,24 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             // four lanes of the head
             const int t0 = P0.tile() * TT + 16 * nb0 + 4 * lg;  // token of element 0 of this wave's block 0
             float smax = -INFINITY;
+            if (P0.tile() * TT + TT <= P0.L) {  // a full tile: no token to mask
 #pragma unroll
-            for (int nb = 0; nb < NB2; ++nb)
+                for (int nb = 0; nb < NB2; ++nb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = t0 + 16 * nb + i < P0.L ? sc[nb][i] * scale_log2 : -INFINITY;
-                    sc[nb][i] = x;
-                    smax = fmaxf(smax, x);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        sc[nb][i] *= scale_log2;
+                        smax = fmaxf(smax, sc[nb][i]);
+                    }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = t0 + 16 * nb + i < P0.L ? sc[nb][i] * scale_log2 : -INFINITY;
+                        sc[nb][i] = x;
+                        smax = fmaxf(smax, x);
+                    }
+            }
             const float mn = fmaxf(m, cross_rows(smax, [](float a, float b) { return fmaxf(a, b); }));
             const float mref = mn == -INFINITY ? 0.f : mn;  // no live token yet (a masked tile): p and alpha are 0
             const float alpha = __builtin_amdgcn_exp2f(m - mref);
