@@ -121,6 +121,8 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
                                                   0, 0, 0);
 }
+// fp16 ones in every operand slot (0x3c00 = 1.0)
+constexpr u32x4 kOnes = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
 __device__ __forceinline__ unsigned pack_h2(_Float16 lo, _Float16 hi) {
     return (unsigned)__builtin_bit_cast(uint16_t, lo) | ((unsigned)__builtin_bit_cast(uint16_t, hi) << 16);
 }
@@ -347,11 +349,13 @@ struct Cfg {
 //
 // Register layouts (query head hq = lane % 16, lane group lg = lane / 16):
 // a score block's result holds tokens 4lg .. 4lg+3 of the block for head hq,
-// so a head's softmax state lives in lanes hq, hq+16, hq+32, hq+48 (their
-// max and sum combined with the permlane swaps); the fp16 probabilities of a
-// 32-token output step are already the B operand of V^T.P^T in the lanes
-// that computed them; the output accumulators hold head hq, channels
-// 16cb + 4lg .. 16cb + 4lg + 3.
+// so a head's running max lives in lanes hq, hq+16, hq+32, hq+48 (combined
+// with the permlane swaps); the fp16 probabilities of a 32-token output step
+// are already the B operand of V^T.P^T in the lanes that computed them; the
+// output accumulators hold head hq, channels 16cb + 4lg .. 16cb + 4lg + 3; and
+// the sum of the weights is one more product of the same step, a row of ones
+// times P^T, so it adds exactly the fp16-rounded weights the output adds, in
+// fp32, and every element of that accumulator holds head hq's sum.
 //
 // LDS tile layouts (fp16 pools, 64-token tiles): K is [NJ][64 tokens][8 ch],
 // so the A operand of a score product (token, 8 channels) is one 16-byte
@@ -583,7 +587,8 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     u32x4 qb[KS];
     f32x4 acc[CB];
     u32x4 pb[PS / 2];  // this tile's probabilities (this wave's tokens) as the output product's operand
-    float m = -INFINITY, lsum = 0.f;
+    float m = -INFINITY;
+    f32x4 accl = {0.f, 0.f, 0.f, 0.f};  // the run's sum of weights for head hq (every element), kept by the matrix cores
 
     // The first tile is requested as soon as its table entries are in; the
     // entries of the next positions are requested after it.
@@ -658,7 +663,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     qb[ks] = hq < NREP ? x : u32x4{0u, 0u, 0u, 0u};
                 }
                 m = -INFINITY;
-                lsum = 0.f;
+                accl = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -731,22 +736,18 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             const float alpha = __builtin_amdgcn_exp2f(m - mref);
             m = mn;
             const float mb = mref - 15.f;  // p enters the products as 2^15 * exp2(s - max)
-            float ps = 0.f;
 #pragma unroll
             for (int q2 = 0; q2 < PS2; ++q2) {
                 _Float16 ph[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    ph[i] = (_Float16)__builtin_amdgcn_exp2f(sc[2 * q2 + (i >> 2)][i & 3] - mb);
-                    ps += (float)ph[i];
-                }
+                for (int i = 0; i < 8; ++i) ph[i] = (_Float16)__builtin_amdgcn_exp2f(sc[2 * q2 + (i >> 2)][i & 3] - mb);
                 pb[q2] = u32x4{pack_h2(ph[0], ph[1]), pack_h2(ph[2], ph[3]), pack_h2(ph[4], ph[5]),
                                pack_h2(ph[6], ph[7])};
             }
-            lsum = lsum * alpha + ps;
             if (__builtin_amdgcn_readfirstlane((int)(__ballot(alpha != 1.0f) != 0))) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+                accl *= alpha;
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -842,11 +843,13 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     }
                 }
 #pragma unroll
-                for (int q2 = 0; q2 < PS2; ++q2)
+                for (int q2 = 0; q2 < PS2; ++q2) {
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
                         acc[cb] = mfma16(u32x4{vr[q2][cb][0].x, vr[q2][cb][0].y, vr[q2][cb][1].x, vr[q2][cb][1].y},
                                          pb[q2], acc[cb]);
+                    accl = mfma16(kOnes, pb[q2], accl);  // the weights' sum: a row of ones times P^T
+                }
             } else {
                 // bytes of (channel c, token t): (c/8)*1024 + (t/16)*128 + (c%8)*16 + t%16; the
                 // codes of tokens past the row's end are already zero (the load wave cleared them
@@ -864,19 +867,21 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                         vr[q2][cb][1] = *reinterpret_cast<const unsigned*>(v + 128);
                     }
 #pragma unroll
-                for (int q2 = 0; q2 < PS2; ++q2)
+                for (int q2 = 0; q2 < PS2; ++q2) {
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
                         const unsigned w0 = vr[q2][cb][0], w1 = vr[q2][cb][1];
                         acc[cb] = mfma16(u32x4{f8x2<false>(w0), f8x2<true>(w0), f8x2<false>(w1), f8x2<true>(w1)},
                                          pb[q2], acc[cb]);
                     }
+                    accl = mfma16(kOnes, pb[q2], accl);  // the weights' sum: a row of ones times P^T
+                }
             }
         }
         float lt = 0.f;
         if (P0.last()) {
             // ---- the two compute waves' states of this run combined (wave 1 -> LDS -> wave 0)
-            if (!loader) lt = tile ? cross_rows(lsum, [](float a, float c) { return a + c; }) : 0.f;
+            if (!loader) lt = tile ? accl[0] : 0.f;
             if (wip == 1) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
