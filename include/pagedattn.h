@@ -112,8 +112,9 @@ pa_status kv_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_po
 
 /*
  * Bytes of device workspace paged_decode_attn needs for these sizes: a fixed
- * region of 32 KiB at the start holding the int32 arrival counters of the
- * split-sequence reduction (one per (row, KV head) of a launch), then the
+ * region of 1 MiB at the start holding the int32 arrival counters of the
+ * split-sequence reduction (one per (row, KV head) of a launch, each on a
+ * 128-byte line of its own), then the
  * fp32 partial results (max, sum, unnormalised output per query head) of up
  * to P = min(64, T) sequence partitions per (row, KV head) of min(num_seqs,
  * 256) rows, T = ceil(W*block_size/64) being the number of 64-token tiles
@@ -180,7 +181,7 @@ pa_status paged_decode_attn(uint16_t *out, const uint16_t *q, const uint16_t *k_
  * zero fill of the array's counter region ahead of it.
  * Limit: calls whose paged_decode_workspace_size() exceeds 32 MiB return
  * PA_ERR_SCRATCH before anything is enqueued (e.g. 32 rows of 12/2/128 heads
- * with tables of up to 300 blocks of 64 tokens need 12.8 MiB).
+ * with tables of up to 300 blocks of 64 tokens need 13.2 MiB).
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents: two calls in flight at the same time on one GPU (different
  * streams, or a graph replayed concurrently with a direct call) race on it

@@ -241,6 +241,9 @@ __device__ __forceinline__ int clamp_block(int blk, int N) {
 constexpr int kMaxRows = 256;    // rows per launch (longer batches are split by the host)
 constexpr int kMaxParts = 64;    // partitions per (row, KV head)
 constexpr int kMaxPending = 4;   // split runs one workgroup may finish (at most its first and last)
+// int32 words between two arrival counters: one counter per 128-byte line, since
+// device-scope atomics on one line are performed one after another
+constexpr int kCounterStride = 32;
 constexpr int kLenMask = 0x3fffffff;     // row length held in LDS ...
 constexpr int kLenNoSlot = 0x40000000;   // ... and a flag: the length exceeds the table, no slot to append into
 
@@ -947,7 +950,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     __syncthreads();
     const int npend = __builtin_amdgcn_readfirstlane(s_npend);
     for (int e = tid; e < npend; e += THREADS) {
-        const int t = __hip_atomic_fetch_add(&counters[s_pend[e]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int t = __hip_atomic_fetch_add(&counters[s_pend[e] * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_pend_np[e] = (t + 1 == s_pend_np[e]) ? s_pend_np[e] : -s_pend_np[e];  // > 0: this workgroup merges
     }
     __syncthreads();
@@ -1022,7 +1025,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                 *reinterpret_cast<f16x4*>(orow + 4 * c4) = oh;
             }
         }
-        if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(&counters[bg * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
     }
 }

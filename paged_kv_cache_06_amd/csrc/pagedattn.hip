@@ -61,10 +61,13 @@ struct Plan {
 };
 
 // Arrival counters: a fixed region at the start of the workspace, one int32
-// per (row, KV head) of a launch. Launches of one call run in order on one
+// per (row, KV head) of a launch, each on a 128-byte line of its own (the
+// arrivals of different (row, KV head)s do not queue behind one another at the
+// memory's atomic unit: measured 13.1 against 13.7 us at uniform 1024, 12.0
+// against 12.4 on the mixed batch). Launches of one call run in order on one
 // stream and each leaves its counters at zero, so they share the region.
 constexpr int kCounterSlots = 8192;
-constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * kCounterStride * 4;  // 1 MiB
 
 Plan make_plan(int B, int Hkv, int bs, int W, int tt) {
     Plan pl;

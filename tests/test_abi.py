@@ -83,13 +83,13 @@ def test_supported_shapes(pa):
 
 
 def test_workspace_size_arithmetic(pa):
-    # a fixed 32 KiB counter region, then B' * partitions * Hq * (D+2) fp32 rounded to 256 B, where
+    # a fixed 1 MiB counter region (8192 counters, one per 128-byte line), then B' * partitions * Hq * (D+2) fp32 rounded to 256 B, where
     # B' = min(B, 256) rows (a bound on one launch's rows) and partitions = min(64, tiles), tiles = ceil(W*bs/64)
     def expect(B, Hq, Hkv, D, bs, W):
         tiles = -(-W * bs // 64)
         parts = min(64, tiles)
         rows = max(1, min(B, 256))
-        return 32768 + -(-(rows * parts * Hq * (D + 2) * 4) // 256) * 256
+        return (1 << 20) + -(-(rows * parts * Hq * (D + 2) * 4) // 256) * 256
 
     for args in [(32, 12, 2, 128, 64, 68), (95, 12, 2, 128, 16, 144), (4, 2, 1, 64, 16, 5), (1, 8, 8, 64, 128, 3),
                  (2, 12, 2, 128, 64, 400), (1000, 12, 2, 128, 16, 300), (600, 64, 32, 64, 16, 8)]:

@@ -4,7 +4,7 @@ filled with a canary byte; after each entry point runs -- the fp16 and E4M3
 decodes, fused, masked and no-workspace forms, the appends, copy-on-write,
 the post-prefill scatter and the debug gather -- both bands of every buffer
 are unchanged, and after every decode the workspace's arrival counters (its
-first 32 KiB) are back at zero. The batch mixes a row long enough to be split
+first MiB) are back at zero. The batch mixes a row long enough to be split
 over many partitions with short, ragged and empty rows."""
 
 import numpy as np
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 PAD = 4096
 CANARY = 0xA5
-COUNTER_BYTES = 32768
+COUNTER_BYTES = 1 << 20
 
 
 @pytest.fixture(scope="module")
