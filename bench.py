@@ -874,7 +874,7 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into profiles/ and exit (no GPU)")
     ap.add_argument("--pmc-copy-mib", type=int, default=256, help="MiB of the calibration copy in those runs")
-    ap.add_argument("--pmc-command", default="", help="the command that made the counter runs")
+    ap.add_argument("--pmc-command", default="", help="the commands that made the counter runs (required with --pmc-summary)")
     ap.add_argument("--pmc-fp8", action="store_true", help="--pmc-summary of an --op fp8 run (E4M3-pool kernel)")
     ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "scatter_prefill", "contrast", "fp8"],
                     help="step: the decode step (default); copy_blocks: the copy-on-write block copy alone; "
@@ -892,6 +892,8 @@ def parse():
 def main():
     args = parse()
     if args.pmc_summary:
+        if not args.pmc_command.strip():
+            sys.exit("--pmc-summary needs --pmc-command: the record names the counter runs it summarises")
         text = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.pmc_copy_mib << 20,
                            args.pmc_command, fp8=args.pmc_fp8)
         os.makedirs(PROFILES, exist_ok=True)

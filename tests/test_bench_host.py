@@ -5,6 +5,7 @@
   dispatch) into HBM bytes per decode launch, each scaled by what the same
   counter reads for a copy of known size: checked on synthetic counter files
   against the arithmetic done by hand;
+* a counter summary is refused without the command that made its runs;
 * a traffic record is used only while the decode kernel's code is the code
   it was taken on (comment edits do not void it, code edits do).
 """
@@ -28,6 +29,16 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_counter_summary_needs_its_command(tmp_path):
+    # a traffic record names the counter runs it summarises: without the
+    # command the summary is refused and nothing is written
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", str(tmp_path / "f"),
+                        str(tmp_path / "w"), "--config", "tiny"], capture_output=True, text=True, timeout=120,
+                       cwd=ROOT)
+    assert r.returncode != 0
+    assert "--pmc-command" in r.stderr
 
 
 def _write_counters(path, counter, rows):
