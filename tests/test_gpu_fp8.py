@@ -153,7 +153,7 @@ def test_decode_fp8_long_rows_split(torch, pa, oracle):
     assert np.array_equal(host(again).view(np.uint16), host(out).view(np.uint16))  # deterministic
 
 
-@pytest.mark.parametrize("name", ["uniform1024", "mixed"])
+@pytest.mark.parametrize("name", ["uniform1024", "uniform4096", "mixed", "high_occupancy"])
 def test_fp8_step_on_qwen_batches(torch, pa, oracle, name):
     # the batch shapes of the fp16 benchmarks with E4M3 pools: the step's
     # quantizing append, then the decode
