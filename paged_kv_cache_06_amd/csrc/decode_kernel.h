@@ -198,8 +198,7 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(const void* src, unsigned dst) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
 }
-// Device-coherent (sc1) stores of the split-sequence partials and plain
-// stores of the output.
+// Device-coherent (sc1) stores of the split-sequence partials.
 __device__ __forceinline__ void st_f32x4_sc1(float* p, f32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
@@ -215,19 +214,24 @@ constexpr int kCoherent = 16;                     // cache-policy bits: sc1
 constexpr int kRawBufferFormat = 0x00020000;      // dword3 of a raw 32-bit buffer resource
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Stores of the output and of the fused append's new K/V: written through
+// (sc1) like the partials, so that the launch leaves no dirty L2 lines for the
+// release at its end to write back (measured 0.2-0.3 us faster at uniform
+// 1024 and on the mixed batch, ~0.2 us slower on the 95-row pool with
+// 16-token blocks).
 __device__ __forceinline__ void st_b64(void* p, unsigned lo, unsigned hi) {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     u32x2 v = {lo, hi};
-    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
-    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"((unsigned)v) : "memory");
+    asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"((unsigned)v) : "memory");
 }
 __device__ __forceinline__ void st_b128(void* p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void st_u8(void* p, unsigned v) {
-    asm volatile("global_store_byte %0, %1, off" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_byte %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int N) {
@@ -1020,9 +1024,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
             const int c4 = tid + i * THREADS;
             if (c4 < NC4) {
                 const f32x4 o = num[i] / den[i] * v_scale;
-                typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                const f16x4 oh = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
-                *reinterpret_cast<f16x4*>(orow + 4 * c4) = oh;
+                st_b64(orow + 4 * c4, pack_h2((_Float16)o.x, (_Float16)o.y), pack_h2((_Float16)o.z, (_Float16)o.w));
             }
         }
         if (tid == 0) __hip_atomic_store(&counters[bg * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
