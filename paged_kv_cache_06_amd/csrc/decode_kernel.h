@@ -198,6 +198,13 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(const void* src, unsigned dst) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
 }
+// The same with the non-temporal (streaming) cache policy, for the K/V tiles,
+// which a launch reads once: measured 9 % faster at uniform 4096 (134 MB per
+// launch), 7 % on the 95-row pool, 4 % at uniform 1024; ~1 % slower on the
+// 28-layer step, whose rows that share a prefix re-read its blocks.
+__device__ __forceinline__ void dma16_nt(const void* src, unsigned dst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(dst) : "memory");
+}
 // Device-coherent (sc1) stores of the split-sequence partials.
 __device__ __forceinline__ void st_f32x4_sc1(float* p, f32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
@@ -573,7 +580,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                               ((size_t)phys * Hkv + s.g()) * (size_t)(D * BS) * E + (size_t)(tok % BS) * 16;
 #pragma unroll
             for (int j = 0; j < NJH; ++j)
-                dma16(src + (size_t)j * (BS * 16), lds_k + (unsigned)((buf * TILE + (hf * NJH + j) * 512) * 2));
+                dma16_nt(src + (size_t)j * (BS * 16), lds_k + (unsigned)((buf * TILE + (hf * NJH + j) * 512) * 2));
         }
         vm_count += NJ;
     };
@@ -585,7 +592,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                           (((size_t)phys * Hkv + s.g()) * (size_t)(D * BS) + (size_t)drow * BS + (size_t)(tok % BS)) * E;
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)  // rows 8jj .. 8jj+7
-            dma16(src + (size_t)jj * (8 * BS) * E, lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
+            dma16_nt(src + (size_t)jj * (8 * BS) * E, lds_v + (unsigned)((buf * TILE + jj * 512) * 2));
         vm_count += NJ;
     };
 
