@@ -618,6 +618,14 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
     }
     if (P0.valid(t_end)) split_of(P0);  // after the first request: not needed for it
     Pos P1 = pos_at(t_begin + 1, P0, true);
+    // With every slot busy, the second K tile is requested in the prologue as well
+    // (with some slots idle, the first tiles land sooner without it).
+    const bool k1_early = Gb == G && P0.valid(t_end) && P0.has_tile();
+    if (loader && k1_early && P1.valid(t_end) && P1.has_tile()) {
+        if (P1.first()) issue_q(P1);
+        issue_k(P1, 1);
+        mk1 = vm_count;
+    }
     Pos P2 = pos_at(t_begin + 2, P1, true);
 
     for (int j = 0; P0.valid(t_end); ++j) {
@@ -655,7 +663,7 @@ __global__ void __launch_bounds__((Cfg<BS, D, NREP, F8>::THREADS)) decode_kernel
                     *new_k_slot(tn));
         }
         if (loader && P1.valid(t_end) && P1.has_tile()) {
-            if (j == 0) {  // the second K tile: requested only now, so that the first one is not queued behind it
+            if (j == 0 && !k1_early) {  // the second K tile, unless the prologue requested it
                 if (P1.first()) issue_q(P1);
                 issue_k(P1, 1);
                 mk1 = vm_count;
